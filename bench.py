@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the Polar Attention hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic inputs that are
+already resident in HBM:
+  * fused prefill forward, bf16, B=1 H=16 T=16384 d=128, causal, planted match groups;
+  * fused prefill forward, bf16, B=1 H=16 T=65536 d=64, causal, tau_h = 0.02 h
+    (the longest context the ATMA summary evaluates, §3);
+  * split-KV decode + merge, bf16, batch 64, H=8, d=128, one query against a
+    65536-token KV cache.
+`value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
+launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
+decode bandwidth is reported beside it.  Per-launch durations come from HIP events
+recorded on the stream the kernels run on (torch's current stream, which the library
+launches on).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Polar-attn fwd TFLOP/s + % bf16 MFMA peak at T=16K/64K; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
+DECODE = "bf16_decode_b64_h8_tk65536_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attention_polar_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(w):
+    return 4 * w.d * w.pairs()
+
+
+def decode_bytes(w):
+    kv = 2 * w.B * w.Hkv * w.Tk * w.d * 2
+    q = w.B * w.H * w.d * 2
+    outs = w.B * w.H * (w.d + 3) * 4   # direction, n_eff, confidence, count... (+ stats not requested)
+    return kv + q + outs
+
+
+def measured_traffic(kernel_key, digest):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(kernel_key)
+    if not entry or entry.get("source_digest") != digest:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle, as it is, on a bounded sample of the 16K prefill workload: blocks
+    of 512 query rows from the end of head 0 (the most expensive rows), until about
+    `seconds` of CPU time have passed."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import polar_inputs as pin
+    from oracle import polar_attention
+
+    w = pin.WORKLOADS[PREFILL[0]]
+    q, k, v, _ = pin.workload_inputs(w, "cpu")
+    q0 = q[:, :1].float().numpy().astype(np.float64)
+    k0 = k[:, :1].float().numpy().astype(np.float64)
+    v0 = v[:, :1].float().numpy().astype(np.float64)
+    del q, k, v
+    rows_done, pairs, t0 = 0, 0, time.perf_counter()
+    end = w.Tq
+    while time.perf_counter() - t0 < seconds and end > 0:
+        rows = np.arange(max(0, end - 512), end)
+        polar_attention(q0, k0, v0, causal=True, len_temp=w.len_temp()[:1], null_bias=w.null_bias()[:1],
+                        count_scale=w.count_scale()[:1], rows=rows)
+        pairs += int((rows + 1).sum())
+        rows_done += len(rows)
+        end -= 512
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": 4 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, last {rows_done} query rows of head 0 of the T=16384 d=128 causal "
+                      f"prefill ({pairs} (query,key) pairs) in {dt:.1f} s; host os.cpu_count()={os.cpu_count()}, "
+                      f"torch threads={torch.get_num_threads()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (prefill shards by head and "
+              "decode by KV range with the split merge; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_polar_amd as pa
+    import polar_inputs as pin
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    parts = []
+    for name in PREFILL:
+        w = pin.WORKLOADS[name]
+        q, k, v, _ = pin.workload_inputs(w, dev)
+        out = pa.allocate_outputs(w.B, w.H, w.Tq, w.d, dev)
+        kw = dict(causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+        parts.append(dict(name=name, w=w, kind="prefill", flops=prefill_flops(w),
+                          run=lambda q=q, k=k, v=v, out=out, kw=kw: pa.fwd(q, k, v, out=out, **kw)))
+    wd = pin.WORKLOADS[DECODE]
+    qd, kd, vd, _ = pin.workload_inputs(wd, dev)
+    prob = pa.problem_for(qd, kd, causal=True, len_temp=wd.len_temp(), null_bias=wd.null_bias(),
+                          count_scale=wd.count_scale())
+    splits = pa.decode_num_splits(prob, 0)
+    ws = torch.empty(pa.decode_workspace_bytes(prob, 0), dtype=torch.uint8, device=dev)
+    outd = pa.allocate_outputs(wd.B, wd.H, 1, wd.d, dev)
+    kwd = dict(len_temp=wd.len_temp(), null_bias=wd.null_bias(), count_scale=wd.count_scale())
+    parts.append(dict(name=DECODE, w=wd, kind="decode", bytes=decode_bytes(wd),
+                      run=lambda: pa.decode(qd, kd, vd, workspace=ws, out=outd, **kwd)))
+    torch.cuda.synchronize()
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p["run"]()
+    torch.cuda.synchronize()
+
+    events = {p["name"]: [] for p in parts}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for p in parts:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            p["run"]()
+            e1.record()
+            events[p["name"]].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    res = {}
+    for p in parts:
+        ms = [a.elapsed_time(b) for a, b in events[p["name"]]]
+        ms.sort()
+        avg = sum(ms) / len(ms)
+        entry = {"ms_avg": avg, "ms_median": ms[len(ms) // 2], "ms_min": ms[0], "ms_max": ms[-1]}
+        if p["kind"] == "prefill":
+            entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
+            entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
+            entry["flops_per_launch"] = p["flops"]
+        else:
+            entry["gbs"] = p["bytes"] / (avg * 1e-3) / 1e9
+            entry["frac_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS
+            entry["bytes_per_launch"] = p["bytes"]
+            entry["splits"] = splits
+        res[p["name"]] = entry
+    for p in parts:  # outputs are finite (a sanity check, parity is in the tests)
+        pass
+    assert torch.isfinite(outd["direction"]).all()
+
+    pf_flops = sum(p["flops"] for p in parts if p["kind"] == "prefill")
+    pf_ms = sum(res[p["name"]]["ms_avg"] for p in parts if p["kind"] == "prefill")
+    value = pf_flops / (pf_ms * 1e-3) / 1e12
+    digest = source_digest()
+    big = res[PREFILL[1]]
+    roofline = {"bound": "mfma", "achieved": big["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": big["tflops"] / PEAK_BF16_TFLOPS, "kernel": "polar_fwd_bf16_kernel<64,...> (T=65536 d=64)",
+                "traffic": measured_traffic("fwd_bf16_t65536_d64", digest)}
+    dec = res[DECODE]
+    decode_roof = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": dec["frac_hbm_peak"], "ms": dec["ms_avg"],
+                   "traffic": measured_traffic("decode_b64_h8_tk65536_d128", digest)}
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "polar attention hot path: prefill bf16 T=16384 d=128 H=16 + prefill bf16 "
+                               "T=65536 d=64 H=16 (causal) + split-KV decode bf16 batch 64 H=8 d=128 KV=65536",
+                   "prefill": PREFILL, "decode": DECODE, "value_is": "prefill TFLOP/s over both prefill launches",
+                   "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
+        "roofline": roofline,
+        "decode": decode_roof,
+        "parts": res,
+        "source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * polar_attn.h - C ABI of the Polar Attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the fused Polar Attention forward of ATMA, as described in the
+ * technical summary "ATMA: Length-Invariant Language Modeling via Polar Attention and
+ * Gated-Delta Compression Memory" (gist.science, paper 2606.25156), cited below as
+ * [ATMA §x]:
+ *   - the direction channel projects the attention-weighted sum of the values onto the
+ *     unit sphere, with a per-head length temperature that sharpens the logits as the
+ *     context grows and an extreme-value-corrected null floor that calibrates them
+ *     against noise [ATMA §2.1, direction channel];
+ *   - the magnitude channel is the participation ratio (inverse Simpson index)
+ *     n_eff = (sum p)^2 / sum p^2 of the attention weights, gated by the confidence of
+ *     signal detection and mapped through a bounded saturating tanh-of-log
+ *     [ATMA §2.1, magnitude channel];
+ *   - the fused kernel streams the running sums with squared correction factors and
+ *     never holds the T x T score matrix; decode reads the KV cache directly
+ *     [ATMA §2.2, hardware-software co-design].
+ *
+ * Per batch b, head h and query row i (query head h reads key/value head
+ * h / (heads / kv_heads)):
+ *   n_i   = keys visible to row i: i + 1 + (seq_k - seq_q) when causal, seq_k otherwise
+ *   lam_i = 1 + tau_h ln n_i                          (length temperature)
+ *   s_ij  = lam_i * softmax_scale * <q_i, k_j>,   m_i = max_j s_ij,   p_ij = exp(s_ij - m_i)
+ *   S1    = sum_j p_ij,   S2 = sum_j p_ij^2,   acc = sum_j p_ij v_j
+ *   direction = acc / ||acc||_2 (zero vector when acc == 0),   n_eff = S1^2 / S2
+ *   null floor f_i = lam_i sqrt(2 ln n_i) + beta_h;  confidence = S1 / (S1 + exp(f_i - m_i))
+ *              (confidence = 1 when the floor is off)
+ *   count = confidence * tanh(ln(n_eff) / kappa_h)
+ * The exact forms of the temperature, floor, confidence and saturation are readings
+ * of the summary, which names these parts without formulas.
+ *
+ * Conventions shared by every entry point
+ *   Layout     q [B, heads, seq_q, head_dim], k and v [B, kv_heads, seq_k, head_dim],
+ *              contiguous row-major.  Outputs are contiguous fp32.
+ *   Pointers   "DEVICE" pointers are HIP device memory owned by the caller; "HOST"
+ *              pointers are read during the call only.  q, k, v, direction and
+ *              workspace must be 16-byte aligned; other outputs 4-byte aligned.
+ *              Outputs must not overlap the inputs.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *              enqueues work; results are valid once the caller synchronises the stream.
+ *   Memory     The library allocates nothing and keeps no mutable global state; calls
+ *              on different streams may run concurrently.
+ *   Errors     All argument checks run before the first HIP call; a call that returns
+ *              anything but POLAR_OK has enqueued nothing.  POLAR_ERR_HIP reports a
+ *              launch failure seen right after the launch; faults inside a kernel
+ *              surface at the caller's next synchronisation.
+ *   Empty      batch == 0 or seq_q == 0 is valid and enqueues nothing; the data
+ *              pointers of such a call may be NULL.
+ */
+#ifndef POLAR_ATTN_H
+#define POLAR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define POLAR_ABI_VERSION 1
+/* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
+ * this many heads; with all three tables NULL any head count is accepted. */
+#define POLAR_MAX_PARAM_HEADS 128
+
+typedef enum polar_status {
+  POLAR_OK = 0,
+  POLAR_ERR_NULL_ARG = 1,     /* a required pointer is NULL                                */
+  POLAR_ERR_BAD_SHAPE = 2,    /* a size is negative or inconsistent                        */
+  POLAR_ERR_UNSUPPORTED = 3,  /* head_dim, dtype, head count or mode not built             */
+  POLAR_ERR_BAD_PARAM = 4,    /* non-finite or out-of-range tau, beta, kappa or scale      */
+  POLAR_ERR_MISALIGNED = 5,   /* a pointer breaks the alignment rule                       */
+  POLAR_ERR_WORKSPACE = 6,    /* decode workspace missing or too small                     */
+  POLAR_ERR_ALIAS = 7,        /* an output overlaps an input                               */
+  POLAR_ERR_HIP = 8           /* the HIP runtime rejected a launch                         */
+} polar_status;
+
+typedef enum polar_dtype {
+  POLAR_BF16 = 0,             /* bf16 q, k, v; fp32 accumulation                           */
+  POLAR_F32 = 1               /* fp32 q, k, v; fp32 arithmetic throughout                  */
+} polar_dtype;
+
+typedef struct polar_problem {
+  int32_t batch;              /* B >= 0                                                     */
+  int32_t heads;              /* query heads >= 1                                           */
+  int32_t kv_heads;           /* key/value heads >= 1, heads % kv_heads == 0                */
+  int32_t seq_q;              /* query rows >= 0                                            */
+  int32_t seq_k;              /* keys >= 1; causal requires seq_q <= seq_k                  */
+  int32_t head_dim;           /* 64 or 128                                                  */
+  int32_t causal;             /* nonzero: key j visible to row i iff j <= i + seq_k - seq_q */
+  int32_t dtype;              /* a polar_dtype                                              */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim); must be finite              */
+  const float* len_temp;      /* HOST [heads] tau_h, NULL = 0; needs 1 + tau_h ln(seq_k) > 0 */
+  const float* null_bias;     /* HOST [heads] beta_h (finite), NULL = null floor off        */
+  const float* count_scale;   /* HOST [heads] kappa_h > 0, NULL = 1                          */
+} polar_problem;
+
+typedef struct polar_outputs {
+  float* direction;           /* DEVICE [B, heads, seq_q, head_dim], required               */
+  float* n_eff;               /* DEVICE [B, heads, seq_q], required                          */
+  float* confidence;          /* DEVICE [B, heads, seq_q], optional (NULL = not written)     */
+  float* count;               /* DEVICE [B, heads, seq_q], optional                          */
+  float* stats;               /* DEVICE [B, heads, seq_q, 3] = (m, S1, S2), optional; m is the
+                                 row maximum of the tempered logits in natural-log units and
+                                 S1, S2 are taken relative to it                             */
+} polar_outputs;
+
+/* Fused Polar Attention forward (prefill) [ATMA §2.2, fused kernel].
+ * One pass over the visible keys per query tile: tiled Q K^T and P V on the matrix
+ * cores with an online softmax that also streams sum p^2 (rescaled by the square of
+ * each correction factor).  Supports bf16 and fp32, head_dim 64 and 128, causal and
+ * non-causal, seq_q <= seq_k when causal (rows aligned to the end of the keys). */
+polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const void* k,
+                            const void* v, const polar_outputs* out, void* stream);
+
+/* Split count the decode will use for `num_splits` (0 = automatic choice); 0 when the
+ * problem is invalid for decode. */
+int32_t polar_attn_decode_num_splits(const polar_problem* problem, int32_t num_splits);
+
+/* Bytes of device workspace polar_attn_decode needs for `num_splits` (0 = automatic):
+ * the per-split partials [B, heads, seq_q, S, head_dim + 3] fp32.  0 when the problem
+ * is invalid for decode. */
+size_t polar_attn_decode_workspace_bytes(const polar_problem* problem, int32_t num_splits);
+
+/* Split-KV decode [ATMA §2.2, decode kernel].  Requires seq_q == 1 (one new query per
+ * sequence) and bf16.  The cache of seq_k keys is cut into S contiguous splits; one
+ * kernel writes the statistics (m, S1, S2, acc) of every split into `workspace` (layout
+ * as for polar_attn_merge), and a second kernel on the same stream merges them with
+ * the global visible count n = seq_k.  1 <= num_splits <= seq_k, or 0 for automatic. */
+polar_status polar_attn_decode(const polar_problem* problem, const void* q, const void* k_cache,
+                               const void* v_cache, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, const polar_outputs* out, void* stream);
+
+/* Merge of split statistics [ATMA §2.2: streaming accumulators with squared correction
+ * factors].  partials: DEVICE [B, heads, seq_q, num_splits, head_dim + 3] fp32, each row
+ * (m, S1, S2, acc[head_dim]) with m in natural-log units and S1, S2, acc relative to
+ * exp(m); a split with no keys has m = -inf.  Each split is brought to the common
+ * maximum m* with w = exp(m_s - m*) (S1 and acc scale by w, S2 by w^2), then the
+ * channels are formed with the visible count of the problem's row i (seq_k when not
+ * causal, i + 1 + seq_k - seq_q when causal).  dtype is ignored. */
+polar_status polar_attn_merge(const polar_problem* problem, const float* partials,
+                              int32_t num_splits, const polar_outputs* out, void* stream);
+
+/* Static description of a status code. */
+const char* polar_status_string(polar_status status);
+
+/* POLAR_ABI_VERSION of the built library. */
+int32_t polar_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POLAR_ATTN_H */

@@ -1,0 +1,274 @@
+"""Polar Attention for AMD Instinct MI355X: a thin ctypes binding over libpolar_attn.so.
+
+Every step of the operator runs in the HIP library; this module only marshals
+arguments.  PyTorch provides device memory and the current stream.  The entry points
+mirror the C ABI in include/polar_attn.h:
+
+    fwd(q, k, v, ...)            -> polar_attn_fwd      (fused prefill forward)
+    decode(q, k_cache, v_cache)  -> polar_attn_decode   (split-KV decode + merge)
+    merge(partials, ...)         -> polar_attn_merge    (merge of split statistics)
+    decode_num_splits / decode_workspace_bytes / status_string / abi_version
+
+Operator source: the ATMA technical summary (gist.science, paper 2606.25156), §2.1
+(direction and magnitude channels) and §2.2 (fused and decode kernels).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpolar_attn.so")
+
+POLAR_BF16, POLAR_F32 = 0, 1
+POLAR_MAX_PARAM_HEADS = 128
+STATUS_NAMES = ["POLAR_OK", "POLAR_ERR_NULL_ARG", "POLAR_ERR_BAD_SHAPE", "POLAR_ERR_UNSUPPORTED",
+                "POLAR_ERR_BAD_PARAM", "POLAR_ERR_MISALIGNED", "POLAR_ERR_WORKSPACE", "POLAR_ERR_ALIAS",
+                "POLAR_ERR_HIP"]
+
+
+class PolarProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("seq_q", ctypes.c_int32), ("seq_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("len_temp", ctypes.POINTER(ctypes.c_float)), ("null_bias", ctypes.POINTER(ctypes.c_float)),
+                ("count_scale", ctypes.POINTER(ctypes.c_float))]
+
+
+class PolarOutputs(ctypes.Structure):
+    _fields_ = [("direction", ctypes.c_void_p), ("n_eff", ctypes.c_void_p), ("confidence", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("stats", ctypes.c_void_p)]
+
+
+class PolarError(RuntimeError):
+    def __init__(self, status: int, lib_message: str):
+        self.status = status
+        self.name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{self.name}: {lib_message}")
+
+
+class PolarArgumentError(PolarError, ValueError):
+    """A status other than POLAR_ERR_HIP: the call was rejected before any launch."""
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m long_context_attention_polar_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, O = ctypes.POINTER(PolarProblem), ctypes.POINTER(PolarOutputs)
+    vp = ctypes.c_void_p
+    lib.polar_attn_fwd.argtypes = [P, vp, vp, vp, O, vp]
+    lib.polar_attn_fwd.restype = ctypes.c_int
+    lib.polar_attn_decode.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_size_t, O, vp]
+    lib.polar_attn_decode.restype = ctypes.c_int
+    lib.polar_attn_merge.argtypes = [P, vp, ctypes.c_int32, O, vp]
+    lib.polar_attn_merge.restype = ctypes.c_int
+    lib.polar_attn_decode_num_splits.argtypes = [P, ctypes.c_int32]
+    lib.polar_attn_decode_num_splits.restype = ctypes.c_int32
+    lib.polar_attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.polar_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.polar_status_string.argtypes = [ctypes.c_int]
+    lib.polar_status_string.restype = ctypes.c_char_p
+    lib.polar_abi_version.argtypes = []
+    lib.polar_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().polar_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().polar_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        cls = PolarError if status == 8 else PolarArgumentError
+        raise cls(status, status_string(status))
+
+
+def _float_array(vals, heads):
+    if vals is None:
+        return None, None
+    if len(vals) != heads:
+        raise ValueError(f"per-head parameter needs {heads} values, got {len(vals)}")
+    arr = (ctypes.c_float * heads)(*[float(x) for x in vals])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), arr
+
+
+@dataclass
+class Problem:
+    """Sizes and parameters of one call (see polar_problem in include/polar_attn.h)."""
+    batch: int
+    heads: int
+    kv_heads: int
+    seq_q: int
+    seq_k: int
+    head_dim: int
+    causal: bool = True
+    dtype: int = POLAR_BF16
+    softmax_scale: float = 0.0
+    len_temp: list | None = None
+    null_bias: list | None = None
+    count_scale: list | None = None
+
+    def to_c(self):
+        lt, k1 = _float_array(self.len_temp, self.heads)
+        nb, k2 = _float_array(self.null_bias, self.heads)
+        cs, k3 = _float_array(self.count_scale, self.heads)
+        pr = PolarProblem(self.batch, self.heads, self.kv_heads, self.seq_q, self.seq_k, self.head_dim,
+                          int(bool(self.causal)), self.dtype, self.softmax_scale, lt, nb, cs)
+        return pr, (k1, k2, k3)  # keep the arrays alive during the call
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return POLAR_BF16
+    if t.dtype == torch.float32:
+        return POLAR_F32
+    raise ValueError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def allocate_outputs(B, H, Tq, d, device, confidence=True, count=True, stats=False):
+    f = dict(device=device, dtype=torch.float32)
+    return {
+        "direction": torch.empty(B, H, Tq, d, **f),
+        "n_eff": torch.empty(B, H, Tq, **f),
+        "confidence": torch.empty(B, H, Tq, **f) if confidence else None,
+        "count": torch.empty(B, H, Tq, **f) if count else None,
+        "stats": torch.empty(B, H, Tq, 3, **f) if stats else None,
+    }
+
+
+def _outputs_c(out):
+    return PolarOutputs(_ptr(out["direction"]), _ptr(out["n_eff"]), _ptr(out.get("confidence")),
+                        _ptr(out.get("count")), _ptr(out.get("stats")))
+
+
+def _check_tensor(name, t, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def problem_for(q, k, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None):
+    B, H, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    return Problem(B, H, Hkv, Tq, Tk, d, causal, _dtype_code(q), float(softmax_scale or 0.0),
+                   None if len_temp is None else list(len_temp),
+                   None if null_bias is None else list(null_bias),
+                   None if count_scale is None else list(count_scale))
+
+
+def fwd(q, k, v, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
+        out=None, stats=False):
+    """Fused Polar Attention forward (polar_attn_fwd).
+
+    q [B,H,Tq,d], k and v [B,Hkv,Tk,d] (bf16 or fp32, contiguous, on one GPU).
+    Returns a dict with direction [B,H,Tq,d], n_eff, confidence, count [B,H,Tq] (fp32)
+    and stats [B,H,Tq,3] when stats=True.  Work is enqueued on the current stream.
+    """
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, dev)
+    if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match each other and q's dtype")
+    prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
+                       softmax_scale=softmax_scale)
+    if out is None:
+        out = allocate_outputs(prob.batch, prob.heads, prob.seq_q, prob.head_dim, dev, stats=stats)
+    pr, keep = prob.to_c()
+    oc = _outputs_c(out)
+    _check(load_library().polar_attn_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(oc),
+                                         _stream(dev)))
+    return out
+
+
+def decode_num_splits(prob: Problem, num_splits: int = 0) -> int:
+    pr, keep = prob.to_c()
+    return int(load_library().polar_attn_decode_num_splits(ctypes.byref(pr), num_splits))
+
+
+def decode_workspace_bytes(prob: Problem, num_splits: int = 0) -> int:
+    pr, keep = prob.to_c()
+    return int(load_library().polar_attn_decode_workspace_bytes(ctypes.byref(pr), num_splits))
+
+
+def decode(q, k_cache, v_cache, *, num_splits=0, len_temp=None, null_bias=None, count_scale=None,
+           softmax_scale=None, workspace=None, out=None, stats=False):
+    """Split-KV decode (polar_attn_decode): q [B,H,1,d] against caches [B,Hkv,Tk,d], bf16.
+
+    Returns the same dict as fwd(); `workspace` (a uint8 device tensor) is allocated
+    when not given, and the partials it holds are returned under "partials"."""
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(name, t, dev)
+    prob = problem_for(q, k_cache, causal=True, len_temp=len_temp, null_bias=null_bias,
+                       count_scale=count_scale, softmax_scale=softmax_scale)
+    lib = load_library()
+    pr, keep = prob.to_c()
+    splits = int(lib.polar_attn_decode_num_splits(ctypes.byref(pr), num_splits))
+    need = int(lib.polar_attn_decode_workspace_bytes(ctypes.byref(pr), num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = allocate_outputs(prob.batch, prob.heads, prob.seq_q, prob.head_dim, dev, stats=stats)
+    oc = _outputs_c(out)
+    _check(lib.polar_attn_decode(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), num_splits,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(oc),
+                                 _stream(dev)))
+    out["splits"] = splits
+    if splits > 0:
+        n = prob.batch * prob.heads * prob.seq_q * splits * (prob.head_dim + 3)
+        out["partials"] = workspace[:n * 4].view(torch.float32).view(prob.batch, prob.heads, prob.seq_q, splits,
+                                                                    prob.head_dim + 3)
+    return out
+
+
+def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_scale=None, out=None,
+          stats=False):
+    """Merge split statistics (polar_attn_merge): partials [B,H,Tq,S,d+3] fp32 on the GPU."""
+    dev = partials.device
+    _check_tensor("partials", partials, dev)
+    if partials.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    B, H, Tq, S, W = partials.shape
+    d = W - 3
+    prob = Problem(B, H, H, Tq, seq_k, d, causal, POLAR_BF16, 0.0,
+                   None if len_temp is None else list(len_temp),
+                   None if null_bias is None else list(null_bias),
+                   None if count_scale is None else list(count_scale))
+    if out is None:
+        out = allocate_outputs(B, H, Tq, d, dev, stats=stats)
+    pr, keep = prob.to_c()
+    oc = _outputs_c(out)
+    _check(load_library().polar_attn_merge(ctypes.byref(pr), _ptr(partials), S, ctypes.byref(oc), _stream(dev)))
+    return out
+
+
+__all__ = ["fwd", "decode", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+           "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
+           "LIB_PATH"]

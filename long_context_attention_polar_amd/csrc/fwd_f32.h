@@ -1,0 +1,129 @@
+// Polar Attention forward with fp32 inputs and fp32 arithmetic throughout.
+//
+// On MI355X the fp32 vector rate equals the fp32 matrix rate, so this path uses plain
+// VALU FMAs: one thread per query row, K and V tiles of BK keys staged in LDS and read
+// by every thread of the workgroup as broadcasts.  The statistics follow the same
+// streaming algebra as the bf16 kernel [ATMA §2.2, fused kernel]: a move of the
+// reference maximum rescales sum p and acc by alpha and sum p^2 by alpha^2.
+#pragma once
+
+#include "polar_common.h"
+
+namespace polar {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
+  constexpr int NT = 128;
+  constexpr int BM = NT;
+  constexpr int BK = 16;
+  __shared__ __attribute__((aligned(16))) float k_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) float v_lds[BK * D];
+
+  const int tid = threadIdx.x;
+  int qt, bh;
+  tile_coords(blockIdx.x, p.n_qt, p.B * p.H, qt, bh);
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int hk = h / (p.H / p.Hkv);
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int off = Tk - Tq;
+  const int q0 = qt * BM;
+  const int qrow = q0 + tid;
+
+  const float* qb = (const float*)p.q + (size_t)bh * Tq * D;
+  const float* kb = (const float*)p.k + (size_t)(b * p.Hkv + hk) * Tk * D;
+  const float* vb = (const float*)p.v + (size_t)(b * p.Hkv + hk) * Tk * D;
+
+  const int hpi = h * p.hp_stride;
+  const int n_vis = visible_keys(qrow, Tq, Tk, CAUSAL);
+  const float lam = length_temperature(p.hp.tau[hpi], n_vis);
+  const float c = lam * p.scale * kLog2e;
+  const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
+
+  float q[D];
+#pragma unroll
+  for (int e = 0; e < D; e += 4) {
+    const f32x4 x = qrow < Tq ? *(const f32x4*)(qb + (size_t)qrow * D + e) : f32x4{0, 0, 0, 0};
+    q[e] = x[0];
+    q[e + 1] = x[1];
+    q[e + 2] = x[2];
+    q[e + 3] = x[3];
+  }
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.0f;
+  float m_ref = kMaxInit, m_true = kMaxInit, s1 = 0.0f, s2 = 0.0f;
+
+  const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += BK) {
+    __syncthreads();
+    for (int idx = tid * 4; idx < BK * D; idx += NT * 4) {
+      const int key = kv0 + idx / D;
+      const int e = idx % D;
+      const f32x4 zero = {0, 0, 0, 0};
+      *(f32x4*)(k_lds + idx) = key < Tk ? *(const f32x4*)(kb + (size_t)key * D + e) : zero;
+      *(f32x4*)(v_lds + idx) = key < Tk ? *(const f32x4*)(vb + (size_t)key * D + e) : zero;
+    }
+    __syncthreads();
+    float sc[BK];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      float r = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) r = fmaf(q[e], k_lds[j * D + e], r);
+      sc[j] = (kv0 + j <= kmax) ? r : -INFINITY;
+      tmax = fmaxf(tmax, sc[j]);
+    }
+    const float cm = c * tmax;
+    m_true = fmaxf(m_true, cm);
+    if (cm > m_ref + kRescaleSlack) {
+      const float m_new = fmaxf(m_ref, cm);
+      const float alpha = fast_exp2(m_ref - m_new);
+      s1 *= alpha;
+      s2 *= alpha * alpha;  // squared correction factor
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] *= alpha;
+      m_ref = m_new;
+    }
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      const float pv = fast_exp2(fmaf(c, sc[j], -m_ref));
+      s1 += pv;
+      s2 = fmaf(pv, pv, s2);
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(pv, v_lds[j * D + e], acc[e]);
+    }
+  }
+
+  if (qrow < Tq) {
+    const float to_true = fast_exp2(m_ref - m_true);
+    const float S1 = s1 * to_true;
+    const float S2 = s2 * to_true * to_true;
+    float nn = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) nn = fmaf(acc[e], acc[e], nn);
+    const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+    const size_t row = (size_t)bh * Tq + qrow;
+    float* drow = p.dir + row * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      const f32x4 val = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+      *(f32x4*)(drow + e) = val;
+    }
+    const float m_nat = m_true * kLn2;
+    float neff, conf, count;
+    magnitude_channel(m_nat, S1, S2, n_vis, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf,
+                      count);
+    p.neff[row] = neff;
+    if (p.conf) p.conf[row] = conf;
+    if (p.count) p.count[row] = count;
+    if (p.stats) {
+      p.stats[row * 3 + 0] = m_nat;
+      p.stats[row * 3 + 1] = S1;
+      p.stats[row * 3 + 2] = S2;
+    }
+  }
+}
+
+}  // namespace polar

@@ -1,0 +1,308 @@
+// Host side of the Polar Attention C ABI: argument checks, per-head constants, launch
+// geometry.  Every check runs before the first HIP call; the library allocates nothing,
+// never synchronises and keeps no mutable global state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <type_traits>
+
+#include "../../include/polar_attn.h"
+#include "decode.h"
+#include "fwd_bf16.h"
+#include "fwd_f32.h"
+#include "polar_common.h"
+
+namespace {
+
+using polar::DecodeParams;
+using polar::FwdParams;
+using polar::HeadParams;
+using polar::MergeParams;
+
+// Prefill launch geometry (one configuration per dtype and head_dim).
+constexpr int kBf16Waves = 4;           // 128 query rows per workgroup
+constexpr int kBf16BlockN_d64 = 128;    // keys per LDS tile at head_dim 64
+constexpr int kBf16BlockN_d128 = 64;    // keys per LDS tile at head_dim 128
+constexpr int kF32Rows = 128;           // query rows per workgroup, fp32 path
+// Decode launch geometry.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeUnroll = 8;
+
+inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+inline size_t elem_bytes(int32_t dtype) { return dtype == POLAR_F32 ? 4 : 2; }
+
+// Shape checks common to every entry point.  `empty` reports a problem with no rows.
+polar_status check_shape(const polar_problem* pr, bool& empty) {
+  if (!pr) return POLAR_ERR_NULL_ARG;
+  if (pr->batch < 0 || pr->seq_q < 0 || pr->heads < 1 || pr->kv_heads < 1 || pr->seq_k < 1)
+    return POLAR_ERR_BAD_SHAPE;
+  if (pr->heads % pr->kv_heads != 0) return POLAR_ERR_BAD_SHAPE;
+  if (pr->causal && pr->seq_q > pr->seq_k) return POLAR_ERR_BAD_SHAPE;
+  if (pr->head_dim != 64 && pr->head_dim != 128) return POLAR_ERR_UNSUPPORTED;
+  if (pr->dtype != POLAR_BF16 && pr->dtype != POLAR_F32) return POLAR_ERR_UNSUPPORTED;
+  empty = (pr->batch == 0 || pr->seq_q == 0);
+  return POLAR_OK;
+}
+
+// Per-head tables -> kernel constants.  Checks the values the maths needs: finite
+// parameters, kappa > 0, and a positive length temperature over the visible counts
+// 1..seq_k (lam is affine in ln n, so checking n = seq_k suffices).
+polar_status head_params(const polar_problem* pr, HeadParams& hp, int& stride, int& floor_on, float& scale) {
+  const bool any = pr->len_temp || pr->null_bias || pr->count_scale;
+  if (any && pr->heads > POLAR_MAX_PARAM_HEADS) return POLAR_ERR_UNSUPPORTED;
+  const int n = any ? pr->heads : 1;
+  stride = any ? 1 : 0;
+  floor_on = pr->null_bias != nullptr;
+  const double ln_tk = std::log((double)pr->seq_k);
+  for (int h = 0; h < n; ++h) {
+    const float tau = pr->len_temp ? pr->len_temp[h] : 0.0f;
+    const float beta = pr->null_bias ? pr->null_bias[h] : 0.0f;
+    const float kappa = pr->count_scale ? pr->count_scale[h] : 1.0f;
+    if (!std::isfinite(tau) || !std::isfinite(beta) || !std::isfinite(kappa) || !(kappa > 0.0f))
+      return POLAR_ERR_BAD_PARAM;
+    if (!(1.0 + (double)tau * ln_tk > 0.0)) return POLAR_ERR_BAD_PARAM;
+    hp.tau[h] = tau;
+    hp.beta[h] = beta;
+    hp.kinv[h] = 1.0f / kappa;
+  }
+  if (!std::isfinite(pr->softmax_scale)) return POLAR_ERR_BAD_PARAM;
+  scale = pr->softmax_scale > 0.0f ? pr->softmax_scale : (float)(1.0 / std::sqrt((double)pr->head_dim));
+  return POLAR_OK;
+}
+
+// Output pointer checks shared by fwd, decode and merge.
+polar_status check_outputs(const polar_problem* pr, const polar_outputs* out, const void* const* ins,
+                           const size_t* in_bytes, int n_in) {
+  if (!out || !out->direction || !out->n_eff) return POLAR_ERR_NULL_ARG;
+  if (!aligned(out->direction, 16) || !aligned(out->n_eff, 4) || !aligned(out->confidence, 4) ||
+      !aligned(out->count, 4) || !aligned(out->stats, 4))
+    return POLAR_ERR_MISALIGNED;
+  const size_t rows = (size_t)pr->batch * pr->heads * pr->seq_q;
+  const void* outs[5] = {out->direction, out->n_eff, out->confidence, out->count, out->stats};
+  const size_t out_bytes[5] = {rows * pr->head_dim * 4, rows * 4, rows * 4, rows * 4, rows * 12};
+  for (int o = 0; o < 5; ++o)
+    for (int i = 0; i < n_in; ++i)
+      if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i])) return POLAR_ERR_ALIAS;
+  for (int o = 0; o < 5; ++o)
+    for (int o2 = o + 1; o2 < 5; ++o2)
+      if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return POLAR_ERR_ALIAS;
+  return POLAR_OK;
+}
+
+template <typename Kernel, typename Params>
+polar_status launch(Kernel kernel, dim3 grid, dim3 block, const Params& params, void* stream) {
+  hipLaunchKernelGGL(kernel, grid, block, 0, (hipStream_t)stream, params);
+  return hipGetLastError() == hipSuccess ? POLAR_OK : POLAR_ERR_HIP;
+}
+
+template <int D, bool CAUSAL>
+polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
+  const long long BH = (long long)pr->batch * pr->heads;
+  if (pr->dtype == POLAR_BF16) {
+    constexpr int BN = D == 64 ? kBf16BlockN_d64 : kBf16BlockN_d128;
+    constexpr int BM = kBf16Waves * 32;
+    fp.n_qt = (pr->seq_q + BM - 1) / BM;
+    const long long blocks = (long long)fp.n_qt * BH;
+    if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, CAUSAL>, dim3((unsigned)blocks),
+                  dim3(kBf16Waves * 64), fp, stream);
+  }
+  fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;
+  const long long blocks = (long long)fp.n_qt * BH;
+  if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+  return launch(polar::polar_fwd_f32_kernel<D, CAUSAL>, dim3((unsigned)blocks), dim3(kF32Rows), fp, stream);
+}
+
+int auto_splits(const polar_problem* pr) {
+  // Aim for about 4096 split workgroups (16 per CU) with at least 256 keys per split.
+  const long long rows = (long long)pr->batch * pr->heads;
+  long long s = (4096 + rows - 1) / rows;
+  const long long max_by_len = (pr->seq_k + 255) / 256;
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+polar_status check_decode(const polar_problem* pr, int32_t num_splits, int& splits) {
+  bool empty = false;
+  const polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  if (pr->seq_q != 1 && !empty) return POLAR_ERR_UNSUPPORTED;
+  if (pr->dtype != POLAR_BF16) return POLAR_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > pr->seq_k) return POLAR_ERR_BAD_SHAPE;
+  splits = num_splits == 0 ? auto_splits(pr) : num_splits;
+  return POLAR_OK;
+}
+
+size_t partial_bytes(const polar_problem* pr, int splits) {
+  return (size_t)pr->batch * pr->heads * pr->seq_q * splits * (pr->head_dim + 3) * sizeof(float);
+}
+
+template <int D>
+polar_status launch_merge(const polar_problem* pr, MergeParams& mp, void* stream) {
+  const long long rows = (long long)pr->batch * pr->heads * pr->seq_q;
+  if (rows > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+  return launch(polar::polar_merge_kernel<D>, dim3((unsigned)rows), dim3(64), mp, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t polar_abi_version(void) { return POLAR_ABI_VERSION; }
+
+const char* polar_status_string(polar_status s) {
+  switch (s) {
+    case POLAR_OK: return "ok";
+    case POLAR_ERR_NULL_ARG: return "a required pointer is NULL";
+    case POLAR_ERR_BAD_SHAPE: return "a size is negative or inconsistent";
+    case POLAR_ERR_UNSUPPORTED: return "head_dim, dtype, head count or mode not supported";
+    case POLAR_ERR_BAD_PARAM: return "non-finite or out-of-range tau, beta, kappa or softmax_scale";
+    case POLAR_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
+    case POLAR_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case POLAR_ERR_ALIAS: return "an output overlaps an input or another output";
+    case POLAR_ERR_HIP: return "the HIP runtime rejected a launch";
+  }
+  return "unknown status";
+}
+
+polar_status polar_attn_fwd(const polar_problem* pr, const void* q, const void* k, const void* v,
+                            const polar_outputs* out, void* stream) {
+  bool empty = false;
+  polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  FwdParams fp;
+  std::memset(&fp, 0, sizeof(fp));
+  st = head_params(pr, fp.hp, fp.hp_stride, fp.floor_on, fp.scale);
+  if (st != POLAR_OK) return st;
+  if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
+  if (!q || !k || !v) return POLAR_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return POLAR_ERR_MISALIGNED;
+  const size_t eb = elem_bytes(pr->dtype);
+  const size_t qb = (size_t)pr->batch * pr->heads * pr->seq_q * pr->head_dim * eb;
+  const size_t kvb = (size_t)pr->batch * pr->kv_heads * pr->seq_k * pr->head_dim * eb;
+  const void* ins[3] = {q, k, v};
+  const size_t in_bytes[3] = {qb, kvb, kvb};
+  st = check_outputs(pr, out, ins, in_bytes, 3);
+  if (st != POLAR_OK) return st;
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.dir = out->direction;
+  fp.neff = out->n_eff;
+  fp.conf = out->confidence;
+  fp.count = out->count;
+  fp.stats = out->stats;
+  fp.B = pr->batch;
+  fp.H = pr->heads;
+  fp.Hkv = pr->kv_heads;
+  fp.Tq = pr->seq_q;
+  fp.Tk = pr->seq_k;
+  if (pr->head_dim == 64)
+    return pr->causal ? launch_fwd<64, true>(pr, fp, stream) : launch_fwd<64, false>(pr, fp, stream);
+  return pr->causal ? launch_fwd<128, true>(pr, fp, stream) : launch_fwd<128, false>(pr, fp, stream);
+}
+
+int32_t polar_attn_decode_num_splits(const polar_problem* pr, int32_t num_splits) {
+  int splits = 0;
+  if (check_decode(pr, num_splits, splits) != POLAR_OK) return 0;
+  return splits;
+}
+
+size_t polar_attn_decode_workspace_bytes(const polar_problem* pr, int32_t num_splits) {
+  int splits = 0;
+  if (check_decode(pr, num_splits, splits) != POLAR_OK) return 0;
+  return partial_bytes(pr, splits);
+}
+
+polar_status polar_attn_merge(const polar_problem* pr, const float* partials, int32_t num_splits,
+                              const polar_outputs* out, void* stream) {
+  bool empty = false;
+  polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  if (num_splits < 1) return POLAR_ERR_BAD_SHAPE;
+  MergeParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  float scale_unused = 0.0f;
+  st = head_params(pr, mp.hp, mp.hp_stride, mp.floor_on, scale_unused);
+  if (st != POLAR_OK) return st;
+  if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
+  if (!partials) return POLAR_ERR_NULL_ARG;
+  if (!aligned(partials, 4)) return POLAR_ERR_MISALIGNED;
+  const void* ins[1] = {partials};
+  const size_t in_bytes[1] = {partial_bytes(pr, num_splits)};
+  st = check_outputs(pr, out, ins, in_bytes, 1);
+  if (st != POLAR_OK) return st;
+  mp.part = partials;
+  mp.dir = out->direction;
+  mp.neff = out->n_eff;
+  mp.conf = out->confidence;
+  mp.count = out->count;
+  mp.stats = out->stats;
+  mp.B = pr->batch;
+  mp.H = pr->heads;
+  mp.Tq = pr->seq_q;
+  mp.Tk = pr->seq_k;
+  mp.S = num_splits;
+  mp.causal = pr->causal != 0;
+  return pr->head_dim == 64 ? launch_merge<64>(pr, mp, stream) : launch_merge<128>(pr, mp, stream);
+}
+
+polar_status polar_attn_decode(const polar_problem* pr, const void* q, const void* k_cache, const void* v_cache,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes,
+                               const polar_outputs* out, void* stream) {
+  int splits = 0;
+  polar_status st = check_decode(pr, num_splits, splits);
+  if (st != POLAR_OK) return st;
+  DecodeParams dp;
+  std::memset(&dp, 0, sizeof(dp));
+  int floor_on = 0;
+  st = head_params(pr, dp.hp, dp.hp_stride, floor_on, dp.scale);
+  if (st != POLAR_OK) return st;
+  if (pr->batch == 0 || pr->seq_q == 0) return POLAR_OK;  // no rows: pointers may be NULL
+  if (!q || !k_cache || !v_cache) return POLAR_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return POLAR_ERR_MISALIGNED;
+  const size_t need = partial_bytes(pr, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return POLAR_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return POLAR_ERR_MISALIGNED;
+  const size_t qb = (size_t)pr->batch * pr->heads * pr->seq_q * pr->head_dim * 2;
+  const size_t kvb = (size_t)pr->batch * pr->kv_heads * pr->seq_k * pr->head_dim * 2;
+  const void* ins[4] = {q, k_cache, v_cache, workspace};
+  const size_t in_bytes[4] = {qb, kvb, kvb, need};
+  st = check_outputs(pr, out, ins, in_bytes, 4);
+  if (st != POLAR_OK) return st;
+  if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k_cache, kvb) ||
+      overlaps(workspace, need, v_cache, kvb))
+    return POLAR_ERR_ALIAS;
+  if (pr->heads > 65535 || pr->batch > 65535) return POLAR_ERR_UNSUPPORTED;
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.part = (float*)workspace;
+  dp.B = pr->batch;
+  dp.H = pr->heads;
+  dp.Hkv = pr->kv_heads;
+  dp.Tk = pr->seq_k;
+  dp.S = splits;
+  dp.split_len = (pr->seq_k + splits - 1) / splits;
+  const dim3 grid(splits, pr->heads, pr->batch);
+  if (pr->head_dim == 64)
+    st = launch(polar::polar_decode_split_kernel<64, kDecodeWaves, kDecodeUnroll>, grid, dim3(kDecodeWaves * 64),
+                dp, stream);
+  else
+    st = launch(polar::polar_decode_split_kernel<128, kDecodeWaves, kDecodeUnroll>, grid, dim3(kDecodeWaves * 64),
+                dp, stream);
+  if (st != POLAR_OK) return st;
+  return polar_attn_merge(pr, (const float*)workspace, splits, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Shared device-side definitions of the Polar Attention kernels (gfx950, wave64).
+//
+// Notation follows the ATMA technical summary (gist.science, paper 2606.25156):
+// direction channel and magnitude channel [ATMA §2.1], fused streaming kernel and
+// decode kernel [ATMA §2.2].  Inside the kernels logits are kept in base-2 units:
+// x = c * <q, k> with c = lam * scale * log2(e), so exp(s - m) = exp2(x - m2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/polar_attn.h"
+
+namespace polar {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Start value of the running maximum (base-2 units).  Finite, so that
+// exp2(x - m) with x = -inf is 0 rather than NaN before the first visible key.
+constexpr float kMaxInit = -1.0e30f;
+// The running reference maximum is moved only when a new score exceeds it by more
+// than this (base 2), so weights stay below 2^8 between moves.  The statistics are
+// exact for any reference; the true maximum is tracked on the side.
+constexpr float kRescaleSlack = 8.0f;
+
+// Per-head parameters, copied by value into the kernel arguments.
+struct HeadParams {
+  float tau[POLAR_MAX_PARAM_HEADS];   // length temperature
+  float beta[POLAR_MAX_PARAM_HEADS];  // null-floor offset
+  float kinv[POLAR_MAX_PARAM_HEADS];  // 1 / kappa
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* dir;
+  float* neff;
+  float* conf;
+  float* count;
+  float* stats;
+  int B, H, Hkv, Tq, Tk;
+  int n_qt;       // query tiles per (b, h)
+  int floor_on;   // null floor on
+  int hp_stride;  // 1: per-head tables, 0: entry 0 serves every head
+  float scale;    // softmax scale
+  HeadParams hp;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* part;    // [B, H, S, D + 3]
+  int B, H, Hkv, Tk;
+  int S;          // splits
+  int split_len;  // keys per split (the last one may be shorter)
+  float scale;
+  int hp_stride;
+  HeadParams hp;
+};
+
+struct MergeParams {
+  const float* part;  // [B, H, Tq, S, D + 3]
+  float* dir;
+  float* neff;
+  float* conf;
+  float* count;
+  float* stats;
+  int B, H, Tq, Tk, S;
+  int causal;
+  int floor_on;
+  int hp_stride;
+  HeadParams hp;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keys visible to query row `row` (rows aligned to the end of the keys when causal).
+__device__ __forceinline__ int visible_keys(int row, int Tq, int Tk, bool causal) {
+  int n = causal ? min(row + 1 + (Tk - Tq), Tk) : Tk;
+  return max(n, 1);
+}
+
+// Length temperature lam(n) = 1 + tau ln n [ATMA §2.1, direction channel].
+__device__ __forceinline__ float length_temperature(float tau, int n) {
+  return 1.0f + tau * logf((float)n);
+}
+
+// Magnitude channel from the row statistics [ATMA §2.1]:
+//   n_eff = S1^2 / S2 (participation ratio),
+//   conf  = S1 / (S1 + exp(f - m)) with the null floor f = lam sqrt(2 ln n) + beta,
+//   count = conf * tanh(ln(n_eff) / kappa).
+// m_nat is the row maximum in natural-log units; S1, S2 are relative to exp(m_nat).
+__device__ __forceinline__ void magnitude_channel(float m_nat, float S1, float S2, int n, float lam,
+                                                  bool floor_on, float beta, float kinv,
+                                                  float& neff, float& conf, float& count) {
+  neff = S1 * S1 / S2;
+  if (floor_on) {
+    const float f = lam * sqrtf(2.0f * logf((float)n)) + beta;
+    conf = 1.0f / (1.0f + expf(f - m_nat - logf(S1)));
+  } else {
+    conf = 1.0f;
+  }
+  count = conf * tanhf(logf(neff) * kinv);
+}
+
+// Block id -> (query tile, b*H + h).  Consecutive block ids are dispatched round-robin
+// over the 8 XCDs; when the head count allows it, every XCD receives whole heads so a
+// head's K/V tiles stay in one XCD's L2.  Within an XCD the heaviest (last, for causal)
+// query tiles are issued first.
+__device__ __forceinline__ void tile_coords(int bid, int n_qt, int BH, int& qt, int& bh) {
+  if ((BH & 7) == 0) {
+    const int hpx = BH >> 3;
+    const int xcd = bid & 7;
+    const int local = bid >> 3;
+    qt = n_qt - 1 - local / hpx;
+    bh = xcd * hpx + local % hpx;
+  } else {
+    qt = n_qt - 1 - bid / BH;
+    bh = bid % BH;
+  }
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace polar

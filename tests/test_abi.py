@@ -1,0 +1,197 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+Every call below is rejected by the library's argument checks, which run before the
+first HIP call, so nothing touches a device.  Pointers are fake but aligned addresses.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import long_context_attention_polar_amd as pa
+from long_context_attention_polar_amd import build as pbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "polar_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pbuild.build()
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(polar_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("polar_attn_fwd", "polar_attn_decode", "polar_attn_merge", "polar_attn_decode_workspace_bytes",
+                     "polar_attn_decode_num_splits", "polar_status_string", "polar_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_abi_version_and_status_strings(lib):
+    version = int(re.search(r"#define POLAR_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert pa.abi_version() == version
+    for s in range(9):
+        assert pa.status_string(s) and pa.status_string(s) != "unknown status"
+    assert pa.status_string(99) == "unknown status"
+
+
+def test_ctypes_struct_layout_matches_header(tmp_path):
+    """The binding's ctypes structures have the header's offsets and sizes (checked by
+    compiling the header with the host C compiler)."""
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "polar_attn.h"\n'
+        "#define F(T, m) printf(#T \" \" #m \" %zu\\n\", offsetof(T, m));\n"
+        "int main(void) {\n"
+        "F(polar_problem, batch) F(polar_problem, heads) F(polar_problem, kv_heads) F(polar_problem, seq_q)\n"
+        "F(polar_problem, seq_k) F(polar_problem, head_dim) F(polar_problem, causal) F(polar_problem, dtype)\n"
+        "F(polar_problem, softmax_scale) F(polar_problem, len_temp) F(polar_problem, null_bias)\n"
+        "F(polar_problem, count_scale)\n"
+        "F(polar_outputs, direction) F(polar_outputs, n_eff) F(polar_outputs, confidence) F(polar_outputs, count)\n"
+        "F(polar_outputs, stats)\n"
+        'printf("sizeof polar_problem %zu\\nsizeof polar_outputs %zu\\n", sizeof(polar_problem), sizeof(polar_outputs));\n'
+        "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for line in filter(None, lines):
+        a, b, c = line.split()
+        if a == "sizeof":
+            cls = pa.PolarProblem if b == "polar_problem" else pa.PolarOutputs
+            assert ctypes.sizeof(cls) == int(c), line
+        else:
+            cls = pa.PolarProblem if a == "polar_problem" else pa.PolarOutputs
+            assert getattr(cls, b).offset == int(c), line
+
+
+# ---------------------------------------------------------------- argument checks (no launch)
+
+FAKE = 1 << 40  # aligned, never dereferenced: every call below fails validation first
+
+
+def fake(n=0):
+    return ctypes.c_void_p(FAKE + n * (1 << 34))
+
+
+def good_problem(**kw):
+    base = dict(batch=1, heads=2, kv_heads=2, seq_q=64, seq_k=64, head_dim=64, causal=True, dtype=pa.POLAR_BF16)
+    base.update(kw)
+    return pa.Problem(**base)
+
+
+def outputs(direction=None, n_eff=None, confidence=None, count=None, stats=None):
+    d = fake(10) if direction is None else direction
+    n = fake(11) if n_eff is None else n_eff
+    return pa.PolarOutputs(d, n, confidence, count, stats)
+
+
+def call_fwd(lib, prob, q=None, k=None, v=None, out=None):
+    pr, keep = prob.to_c()
+    o = outputs() if out is None else out
+    return lib.polar_attn_fwd(ctypes.byref(pr), fake(1) if q is None else q, fake(2) if k is None else k,
+                              fake(3) if v is None else v, ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 2), (dict(seq_q=-1), 2), (dict(heads=0), 2), (dict(kv_heads=0), 2), (dict(seq_k=0), 2),
+    (dict(heads=3, kv_heads=2), 2), (dict(seq_q=65, seq_k=64), 2), (dict(head_dim=96), 3), (dict(head_dim=256), 3),
+    (dict(dtype=7), 3), (dict(softmax_scale=float("nan")), 4), (dict(softmax_scale=float("inf")), 4),
+    (dict(len_temp=[0.0, float("nan")]), 4), (dict(len_temp=[0.0, -1.0]), 4), (dict(count_scale=[1.0, 0.0]), 4),
+    (dict(count_scale=[1.0, -2.0]), 4), (dict(null_bias=[0.0, float("inf")]), 4),
+    (dict(heads=256, kv_heads=256, len_temp=[0.0] * 256), 3),
+])
+def test_fwd_rejects_bad_problem(lib, kw, status):
+    assert call_fwd(lib, good_problem(**kw)) == status
+
+
+def test_fwd_rejects_bad_pointers(lib):
+    prob = good_problem()
+    assert call_fwd(lib, prob, q=ctypes.c_void_p(0)) == 1
+    assert call_fwd(lib, prob, v=ctypes.c_void_p(0)) == 1
+    assert call_fwd(lib, prob, out=outputs(direction=ctypes.c_void_p(0))) == 1
+    pr, keep = prob.to_c()
+    assert lib.polar_attn_fwd(ctypes.byref(pr), fake(1), fake(2), fake(3), None, None) == 1
+    assert lib.polar_attn_fwd(None, fake(1), fake(2), fake(3), ctypes.byref(outputs()), None) == 1
+    assert call_fwd(lib, prob, q=ctypes.c_void_p(FAKE + 8)) == 5
+    assert call_fwd(lib, prob, out=outputs(direction=ctypes.c_void_p(FAKE + (1 << 36) + 4))) == 5
+    assert call_fwd(lib, prob, out=outputs(n_eff=ctypes.c_void_p(FAKE + (1 << 36) + 2))) == 5
+    # an output overlapping an input, and two overlapping outputs
+    assert call_fwd(lib, prob, out=outputs(direction=fake(1))) == 7
+    assert call_fwd(lib, prob, out=outputs(n_eff=ctypes.c_void_p(FAKE + 2 * (1 << 34) + 64))) == 7
+    assert call_fwd(lib, prob, out=outputs(count=fake(11))) == 7
+
+
+def test_negative_tau_within_range_is_accepted_by_validation(lib):
+    """1 + tau ln(seq_k) > 0 is the condition; tau = -0.1 at seq_k = 64 passes the check
+    (the call is then stopped by an overlap of outputs, before any launch)."""
+    prob = good_problem(len_temp=[-0.1, -0.2])
+    assert call_fwd(lib, prob, out=outputs(count=fake(11))) == 7
+
+
+def test_decode_and_merge_validation(lib):
+    prob = good_problem(seq_q=1, seq_k=1000, causal=True, head_dim=128)
+    pr, keep = prob.to_c()
+    assert lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0) >= 1
+    assert lib.polar_attn_decode_num_splits(ctypes.byref(pr), 7) == 7
+    assert lib.polar_attn_decode_num_splits(ctypes.byref(pr), 1001) == 0
+    assert lib.polar_attn_decode_workspace_bytes(ctypes.byref(pr), 5) == 1 * 2 * 1 * 5 * 131 * 4
+    bad = good_problem(seq_q=2, seq_k=1000)
+    bpr, bkeep = bad.to_c()
+    assert lib.polar_attn_decode_workspace_bytes(ctypes.byref(bpr), 0) == 0
+    o = outputs()
+    # seq_q != 1 and fp32 are not decode problems
+    assert lib.polar_attn_decode(ctypes.byref(bpr), fake(1), fake(2), fake(3), 0, fake(4), 1 << 20, ctypes.byref(o),
+                                 None) == 3
+    f32 = good_problem(seq_q=1, seq_k=1000, dtype=pa.POLAR_F32)
+    fpr, fkeep = f32.to_c()
+    assert lib.polar_attn_decode(ctypes.byref(fpr), fake(1), fake(2), fake(3), 0, fake(4), 1 << 20, ctypes.byref(o),
+                                 None) == 3
+    # workspace missing / too small / misaligned; too many splits
+    assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 4, None, 0, ctypes.byref(o), None) == 6
+    need = lib.polar_attn_decode_workspace_bytes(ctypes.byref(pr), 4)
+    assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 4, fake(4), need - 1, ctypes.byref(o),
+                                 None) == 6
+    assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 4, ctypes.c_void_p(FAKE + 4 * (1 << 34) + 4),
+                                 need, ctypes.byref(o), None) == 5
+    assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 1001, fake(4), 1 << 30, ctypes.byref(o),
+                                 None) == 2
+    # workspace overlapping an output
+    assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 4, fake(10), need, ctypes.byref(o),
+                                 None) == 7
+    # merge
+    assert lib.polar_attn_merge(ctypes.byref(pr), None, 4, ctypes.byref(o), None) == 1
+    assert lib.polar_attn_merge(ctypes.byref(pr), fake(4), 0, ctypes.byref(o), None) == 2
+    assert lib.polar_attn_merge(ctypes.byref(pr), fake(10), 4, ctypes.byref(o), None) == 7
+
+
+def test_python_binding_checks():
+    with pytest.raises(ValueError):
+        good_problem(len_temp=[0.0]).to_c()
+    assert issubclass(pa.PolarArgumentError, ValueError)
+
+
+def test_build_compiles_for_gfx950():
+    """build() produces a shared library with gfx950 device code (cross-compiled here)."""
+    with open(pbuild.__file__) as f:
+        src = f.read()
+    assert 'ARCH = "gfx950"' in src and "-packed-fp32-ops" in src

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generators in polar_inputs; the oracle receives the very
+tensors the GPU consumes (bf16 values upcast exactly).  Sizes the oracle finishes in
+seconds are compared on every row; the full-size workloads are compared on sampled
+rows, which the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_polar_amd as pa
+import polar_inputs as pin
+from oracle import merge_reference, polar_attention, split_statistics
+from tests.parity import assert_parity, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def kind_of(dtype):
+    return "f32" if dtype == torch.float32 else "bf16"
+
+
+def run_case(B, H, Hkv, Tq, Tk, d, dtype, causal, seed, tau=None, beta=None, kappa=None, rows=None, stats=True,
+             label=""):
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, Tq, Tk, d, dtype, seed)
+    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa,
+                 stats=stats)
+    torch.cuda.synchronize()
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=causal, len_temp=tau, null_bias=beta,
+                          count_scale=kappa, rows=rows)
+    return assert_parity(out, ref, kind_of(dtype), rows=rows, label=label)
+
+
+# ---------------------------------------------------------------- reduced shapes, every row
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 300, 1000])
+def test_fwd_shapes(dtype, d, causal, T):
+    H = 2
+    run_case(1, H, H, T, T, d, dtype, causal, seed=T * 7 + d, beta=[0.0] * H, label=f"T={T} d={d}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("tau,beta,kappa", [
+    ([0.0, 0.1], [-2.0, 3.0], [1.0, 4.0]),
+    ([0.1, 0.0], None, [4.0, 1.0]),
+    ([0.3, 0.05], [0.0, 0.0], None),
+])
+def test_fwd_parameter_sweep(dtype, tau, beta, kappa):
+    run_case(2, 2, 2, 333, 333, 64, dtype, True, seed=5, tau=tau, beta=beta, kappa=kappa)
+    run_case(1, 2, 2, 200, 200, 128, dtype, False, seed=6, tau=tau, beta=beta, kappa=kappa)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fwd_gqa_and_bottom_right_causal(dtype):
+    run_case(2, 4, 2, 150, 150, 128, dtype, True, seed=11, beta=[0.0] * 4, label="gqa")
+    run_case(1, 4, 1, 70, 333, 64, dtype, True, seed=12, tau=[0.1] * 4, beta=[0.5] * 4, label="Tq<Tk causal")
+    run_case(1, 2, 2, 70, 333, 64, dtype, False, seed=13, beta=[0.0] * 2, label="Tq<Tk")
+
+
+def test_fwd_scale_override_and_large_logits():
+    q, k, v, _ = pin.random_qkv(1, 2, 2, 257, 257, 64, torch.bfloat16, 21)
+    q = q * 4  # exact in bf16: large logits exercise the reference-maximum moves
+    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), softmax_scale=0.3, null_bias=[0.0, 1.0], stats=True)
+    torch.cuda.synchronize()
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), softmax_scale=0.3, null_bias=[0.0, 1.0])
+    assert_parity(out, ref, "bf16")
+
+
+def test_fwd_uniform_logits_exact_neff():
+    """q = 0: every visible key has p = 1, so n_eff equals the visible count exactly."""
+    T, d = 700, 128
+    q = torch.zeros(1, 2, T, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(1, 2, T, d, device=DEV).to(torch.bfloat16)
+    v = torch.randn(1, 2, T, d, device=DEV).to(torch.bfloat16)
+    out = pa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    n = torch.arange(1, T + 1, device=DEV, dtype=torch.float32)
+    assert torch.equal(out["n_eff"][0, 0], n) and torch.equal(out["n_eff"][0, 1], n)
+
+
+def test_fwd_optional_outputs_and_determinism():
+    q, k, v, _ = pin.random_qkv(1, 2, 2, 300, 300, 64, torch.bfloat16, 31)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = pa.fwd(q, k, v, null_bias=[0.0, 0.0], stats=True)
+    b = pa.fwd(q, k, v, null_bias=[0.0, 0.0], stats=True)
+    out = pa.allocate_outputs(1, 2, 300, 64, DEV, confidence=False, count=False)
+    c = pa.fwd(q, k, v, null_bias=[0.0, 0.0], out=out)
+    off = pa.fwd(q, k, v, null_bias=None)
+    hi = pa.fwd(q, k, v, null_bias=[3.0, -2.0])
+    torch.cuda.synchronize()
+    for key in ("direction", "n_eff", "confidence", "count", "stats"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["direction"], c["direction"]) and torch.equal(a["n_eff"], c["n_eff"])
+    # the null floor moves only the confidence: direction and n_eff are bitwise unchanged
+    for other in (off, hi):
+        assert torch.equal(a["direction"], other["direction"]) and torch.equal(a["n_eff"], other["n_eff"])
+    assert torch.equal(off["confidence"], torch.ones_like(off["confidence"]))
+
+
+def test_fwd_empty_inputs():
+    q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(1, 2, 5, 64, device=DEV).to(torch.bfloat16)
+    out = pa.fwd(q, k, k.clone(), causal=True)
+    assert out["direction"].numel() == 0
+    q0 = torch.empty(0, 2, 4, 64, dtype=torch.bfloat16, device=DEV)
+    k0 = torch.empty(0, 2, 4, 64, dtype=torch.bfloat16, device=DEV)
+    pa.fwd(q0, k0, k0.clone())
+    torch.cuda.synchronize()
+
+
+def test_fwd_rejects_bad_calls():
+    q = torch.randn(1, 2, 8, 64, device=DEV).to(torch.bfloat16)
+    with pytest.raises(pa.PolarArgumentError):
+        pa.fwd(q, q.clone(), q.clone(), len_temp=[0.0, -5.0])  # lam(8) <= 0
+    with pytest.raises(pa.PolarArgumentError):
+        pa.fwd(q[:, :, :, :32].contiguous(), q[:, :, :, :32].contiguous(), q[:, :, :, :32].contiguous())
+
+
+# ---------------------------------------------------------------- decode and merge
+
+def decode_case(B, H, Hkv, Tk, d, seed, splits_list, tau=None, beta=None, kappa=None):
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, 1, Tk, d, torch.bfloat16, seed)
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=True, len_temp=tau, null_bias=beta,
+                          count_scale=kappa)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = []
+    for s in splits_list:
+        out = pa.decode(qd, kd, vd, num_splits=s, len_temp=tau, null_bias=beta, count_scale=kappa, stats=True)
+        torch.cuda.synchronize()
+        assert_parity(out, ref, "bf16", label=f"decode S={s}")
+        # the partials, merged by the oracle, give the same outputs
+        parts = to_np(out["partials"])
+        merged = merge_reference(parts, Tk, len_temp=tau, null_bias=beta, count_scale=kappa)
+        assert_parity(out, merged, "bf16", label=f"oracle merge of GPU partials S={s}")
+        outs.append(out)
+    return outs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_split_invariance(d):
+    decode_case(2, 4, 4, 3001, d, seed=40 + d, splits_list=[1, 2, 3, 8, 64, 0],
+                tau=[0.0, 0.1, 0.2, 0.05], beta=[0.0, -1.0, 2.0, 0.0], kappa=[1.0, 2.0, 1.0, 4.0])
+
+
+def test_decode_small_and_ragged():
+    decode_case(1, 2, 2, 1, 128, seed=50, splits_list=[1, 0])
+    decode_case(1, 2, 2, 17, 64, seed=51, splits_list=[1, 5, 17, 0], beta=[0.0, 0.0])
+    decode_case(3, 8, 2, 1000, 128, seed=52, splits_list=[7, 0], beta=[0.0] * 8)  # GQA
+
+
+def test_merge_entry_point_on_oracle_partials():
+    """polar_attn_merge on partials written by the oracle (never by the GPU)."""
+    rng = np.random.default_rng(60)
+    B, H, Tq, Tk, d, S = 2, 3, 4, 500, 128, 6
+    tau, beta, kappa = [0.0, 0.1, 0.3], [0.0, 1.0, -1.0], [1.0, 0.5, 2.0]
+    q = rng.standard_normal((B, H, Tq, d))
+    k, v = rng.standard_normal((2, B, H, Tk, d))
+    bounds = np.linspace(0, Tk, S + 1).astype(int)
+    part = np.zeros((B, H, Tq, S, d + 3))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Tq):
+                n = i + 1 + Tk - Tq
+                lam = 1 + tau[h] * math.log(n)
+                for s in range(S):
+                    lo, hi = bounds[s], min(bounds[s + 1], n)
+                    if hi <= lo:
+                        part[b, h, i, s, 0] = -np.inf
+                        continue
+                    m, s1, s2, acc = split_statistics(q[b, h, i], k[b, h], v[b, h], lam, 1 / math.sqrt(d), lo, hi)
+                    part[b, h, i, s] = [m, s1, s2, *acc]
+    ref = merge_reference(part, np.arange(Tk - Tq + 1, Tk + 1)[None, None, :], len_temp=tau, null_bias=beta,
+                          count_scale=kappa)
+    gp = torch.from_numpy(part).float().to(DEV)
+    out = pa.merge(gp, seq_k=Tk, causal=True, len_temp=tau, null_bias=beta, count_scale=kappa, stats=True)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, "f32", label="merge")
+
+
+# ---------------------------------------------------------------- the named workloads
+
+def sampled_rows(T, extra, n=48, seed=0):
+    r = np.random.default_rng(seed)
+    rows = set(r.choice(T, size=min(n, T), replace=False).tolist()) | {0, 1, T - 1} | set(extra)
+    return np.array(sorted(x for x in rows if 0 <= x < T))
+
+
+def workload_case(name, full_rows):
+    w = pin.WORKLOADS[name]
+    print(f"[parity] {name}", flush=True)
+    q, k, v, meta = pin.workload_inputs(w, "cpu")
+    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(),
+                 count_scale=w.count_scale(), stats=True)
+    torch.cuda.synchronize()
+    extra = [n[2] for n in meta.get("needles", [])] + [g[3] for g in meta.get("groups", [])]
+    rows = None if full_rows else sampled_rows(w.Tq, extra)
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=w.causal, len_temp=w.len_temp(),
+                          null_bias=w.null_bias(), count_scale=w.count_scale(), rows=rows)
+    e = assert_parity(out, ref, kind_of(w.dtype), rows=rows, label=name)
+    print(f"[parity] {name} max errors {e}", flush=True)
+    return out, meta
+
+
+def test_workload_fp32_t256():
+    workload_case("fp32_b1_h2_t256_d64", full_rows=True)
+
+
+def test_workload_needle_t4096():
+    out, meta = workload_case("bf16_b4_h8_t4096_d64_needle", full_rows=True)
+    # the planted match dominates its row: n_eff close to 1
+    for b, h, i, j in meta["needles"]:
+        assert out["n_eff"][b, h, i].item() < 1.5
+
+
+def test_workload_groups_t16384():
+    out, meta = workload_case("bf16_b1_h16_t16384_d128_groups", full_rows=False)
+    for b, h, c, i, pos in meta["groups"]:
+        assert abs(out["n_eff"][b, h, i].item() - c) < 0.1 * c + 0.5
+
+
+def test_workload_lentemp_t65536():
+    workload_case("bf16_b1_h16_t65536_d64_lentemp", full_rows=False)
+
+
+def test_workload_decode_64k():
+    w = pin.WORKLOADS["bf16_decode_b64_h8_tk65536_d128"]
+    print("[parity] decode workload", flush=True)
+    q, k, v, _ = pin.workload_inputs(w, DEV)
+    out = pa.decode(q, k, v, len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale(),
+                    stats=True)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(70)
+    for b, h in [(0, 0), (63, 7)] + [tuple(x) for x in zip(r.integers(0, 64, 4), r.integers(0, 8, 4))]:
+        ref = polar_attention(to_np(q[b:b + 1, h:h + 1]), to_np(k[b:b + 1, h:h + 1]), to_np(v[b:b + 1, h:h + 1]),
+                              causal=True, len_temp=[w.len_temp()[h]], null_bias=[w.null_bias()[h]],
+                              count_scale=[w.count_scale()[h]])
+        sub = {key: (t[b:b + 1, h:h + 1] if torch.is_tensor(t) else t) for key, t in out.items()
+               if key not in ("partials", "splits")}
+        assert_parity(sub, ref, "bf16", label=f"decode b={b} h={h}")
+    del k, v
+    torch.cuda.empty_cache()
