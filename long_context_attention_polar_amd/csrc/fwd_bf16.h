@@ -7,49 +7,89 @@
 //
 // Work decomposition
 //   * A workgroup of NW waves owns BM = 32 * NW query rows of one (b, h); each wave
-//     owns 32 rows.  Keys stream through LDS in tiles of BN, double-buffered: the next
-//     tile's global loads are issued before the current tile is computed and written
-//     to the other LDS buffer afterwards, one barrier per tile.
+//     owns 32 rows.  Keys stream through LDS in tiles of BN = 64 rows, double-buffered,
+//     with direct global->LDS loads (no registers, no LDS store instructions): the loads
+//     of tile t+1 are in flight while tile t is computed, and one barrier per tile
+//     publishes them.  K and V stay row-major in LDS; the 16-byte chunks of a row are
+//     XOR-swizzled so both read patterns below are free of bank conflicts.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (A = K rows from LDS, B = the wave's Q^T fragment held in registers).  In the
-//     32x32 accumulator layout lane l then holds query (l % 32) and 16 of every 32 keys,
-//     so a row's maximum and sums are one cross-half exchange away, and its
-//     correction factor is a per-lane scalar.
-//   * The output is accumulated transposed, O^T += V^T P^T.  The probabilities are
-//     already where the B operand needs them (the lane's own query, 8 keys per k-step)
-//     once the keys of each 16-key step are taken in the order
-//     0-3, 8-11, 4-7, 12-15; V^T is stored in LDS in that order, so the A operand is
-//     one 16-byte LDS read per lane.
-//   * sum p and sum p^2 are per-lane partial sums in fp32, taken from the fp32 p before
-//     it is rounded to bf16 for the P V product; the two halves of the wave are added
-//     once, in the epilogue.
+//     32x32 accumulator layout lane l holds query (l % 32) and 16 of every 32 keys, so a
+//     row's statistics are per-lane scalars split over two lanes (l, l ^ 32).
+//   * The output is accumulated transposed, O^T += V^T P^T.  The probabilities are used
+//     in place as the B operand once the keys of each 16-key step are taken in the
+//     order 0-3, 8-11, 4-7, 12-15; the matching V^T operand comes straight from the
+//     row-major V tile through two ds_read_b64_tr_b16 transpose reads, each delivering
+//     four consecutive keys of one dimension to a lane.
+//   * The reference maximum moves only when a score exceeds it by more than 2^8 (base 2),
+//     decided for the whole wave with one ballot; only then are the two halves of a row
+//     exchanged and sum p, sum p^2 (by alpha^2) and acc rescaled.  The true maximum is
+//     tracked on the side for the reported statistics.
+//   * sum p and sum p^2 are fp32 per-lane partial sums (four of each, to keep the
+//     dependency chains short), taken from the fp32 p before it is rounded to bf16 for
+//     the P V product; they are combined once, in the epilogue.
 #pragma once
 
 #include "polar_common.h"
 
 namespace polar {
 
-// Position, inside a 16-key step of V^T in LDS, of key group g (4 keys each).
-__device__ __forceinline__ int vt_group_pos(int g) { return (g == 1) ? 2 : (g == 2) ? 1 : g; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define POLAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define POLAR_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
 
-template <int D, int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void polar_fwd_bf16_kernel(const FwdParams p) {
-  constexpr int NT = NW * 64;
+// XOR swizzle of the 16-byte chunks of an LDS row of K or V (row = key index in the
+// tile).  D = 64: two rows share the 64 banks; the chunk index is permuted by a map of
+// (row / 2) whose consecutive even/odd pairs land in different chunk pairs.  D = 128:
+// a row spans all banks; the chunk index is XORed with a permutation of (row % 16)
+// whose four consecutive rows fall into four different quarters.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 64) {
+    const int e = (row >> 1) & 7;
+    return (e >> 1) | ((e & 1) << 2);
+  } else {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  }
+}
+
+// Issue the direct global->LDS loads of one BN x D bf16 tile whose first row is key
+// kv0.  Every wave-wide instruction fills 1 KiB of LDS (lane i -> bytes [16 i, 16 i + 16));
+// the lane chooses its global chunk so that the LDS image is the swizzled tile.  Rows
+// past the last key repeat the last key (their scores are masked).
+template <int D, int BN, int NW>
+__device__ __forceinline__ void load_tile(const __bf16* src, int kv0, int Tk, __bf16* dst, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int INSTR = BN * D * 2 / 1024;
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int r = 0; r < INSTR / NW; ++r) {
+    const int i = wave + r * NW;
+    const int idx = i * 64 + lane;
+    const int row = idx / CPR;
+    const int lc = (idx % CPR) ^ chunk_swizzle<D>(row);
+    const int key = min(kv0 + row, Tk - 1);
+    __builtin_amdgcn_global_load_lds(POLAR_GLOBAL(src + (size_t)key * D + lc * 8), POLAR_LDS(dst + i * 512), 16, 0,
+                                     0);
+  }
+}
+
+template <int D, int NW, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_fwd_bf16_kernel(
+    const FwdParams p) {
+  constexpr int BN = 64;
   constexpr int BM = NW * 32;
-  constexpr int KSTR = D + 8;          // K row stride in LDS (elements)
-  constexpr int VSTR = BN + 8;         // V^T row stride in LDS (elements)
-  constexpr int MB = BN / 32;          // 32-key blocks per tile
-  constexpr int KS = D / 16;           // k-steps of Q K^T
-  constexpr int DM = D / 32;           // 32-wide d blocks of P V
-  constexpr int PS = BN / 16;          // k-steps of P V
-  constexpr int KCHUNKS = BN * D / 8;  // 16-byte chunks per K tile
-  constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-  constexpr int VUNITS = (BN / 4) * (D / 8);  // (4 keys x 8 dims) units per V tile
-  constexpr int VPT = (VUNITS + NT - 1) / NT;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  constexpr int MB = BN / 32;  // 32-key blocks per tile
+  constexpr int KS = D / 16;   // k-steps of Q K^T
+  constexpr int DM = D / 32;   // 32-wide d blocks of P V
+  constexpr int PS = BN / 16;  // k-steps of P V
+  static_assert(D == 64 || D == 128, "head_dim");
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VSTR];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_buf0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_buf1[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_buf0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_buf1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -71,12 +111,19 @@ __global__ __launch_bounds__(NW * 64) void polar_fwd_bf16_kernel(const FwdParams
   const __bf16* kb = (const __bf16*)p.k + (size_t)(b * p.Hkv + hk) * Tk * D;
   const __bf16* vb = (const __bf16*)p.v + (size_t)(b * p.Hkv + hk) * Tk * D;
 
+  const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int wave_kmax = CAUSAL ? min(q0 + wave * 32 + 31 + off, Tk - 1) : Tk - 1;
+
+  // Start the first tile's loads before anything else.
+  load_tile<D, BN, NW>(kb, 0, Tk, k_buf0, wave, lane);
+  load_tile<D, BN, NW>(vb, 0, Tk, v_buf0, wave, lane);
+
   const int hpi = h * p.hp_stride;
   const int n_vis = visible_keys(qrow, Tq, Tk, CAUSAL);
   const float lam = length_temperature(p.hp.tau[hpi], n_vis);
   const float c = lam * p.scale * kLog2e;
-  // Largest key index this lane's query may see.
-  const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
+  const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;  // last key this row may see
 
   // Q^T fragments: lane holds query qrow, dims ks*16 + 8*half + [0, 8).
   bf16x8 qf[KS];
@@ -90,121 +137,89 @@ __global__ __launch_bounds__(NW * 64) void polar_fwd_bf16_kernel(const FwdParams
     }
   }
 
-  const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
-  const int ntiles = (kv_end + BN - 1) / BN;
-  const int first_mask_tile = CAUSAL ? (q0 + off + 1) / BN : Tk / BN;
-  const int wave_kmax = CAUSAL ? min(q0 + wave * 32 + 31 + off, Tk - 1) : Tk - 1;
+  // LDS element offsets of this lane's operand reads (same for both buffers).
+  // K (A operand of S^T): row mb*32 + col, logical chunk 2*ks + half.
+  const int k_sw = chunk_swizzle<D>(col);
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * D + (((2 * ks + half) ^ k_sw) << 3);
+  // V (A operand of O^T via transpose reads): in the 16-lane group g = lane / 16 the lane
+  // points at key (4 * half + gi / 4) [+ 8 for the second read] and dims
+  // dm*32 + 16*(g & 1) + 4*(gi & 3) .. + 3.
+  const int gi = lane & 15;
+  const int g = lane >> 4;
+  int v_off[2][DM];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * half + (gi >> 2);
+    const int sw = chunk_swizzle<D>(row);
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+      const int lchunk = 4 * dm + 2 * (g & 1) + ((gi & 3) >> 1);
+      v_off[r][dm] = row * D + ((lchunk ^ sw) << 3) + 4 * (gi & 1);
+    }
+  }
 
-  // ---- global -> registers -> LDS staging of one K/V tile
-  u32x4 kreg[KPT];
-  u32x4 vreg[VPT][4];
-  auto load_tile = [&](int t) {
-    const int kv0 = t * BN;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int cidx = tid + r * NT;
-      if (KCHUNKS % NT == 0 || cidx < KCHUNKS) {
-        const int row = cidx / (D / 8), c8 = cidx % (D / 8);
-        const int key = kv0 + row;
-        kreg[r] = key < Tk ? *(const u32x4*)(kb + (size_t)key * D + c8 * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < VPT; ++r) {
-      const int u = tid + r * NT;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int dch = u % (D / 8), kg = u / (D / 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kv0 + 4 * kg + j;
-          vreg[r][j] = key < Tk ? *(const u32x4*)(vb + (size_t)key * D + dch * 8) : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int cidx = tid + r * NT;
-      if (KCHUNKS % NT == 0 || cidx < KCHUNKS) {
-        const int row = cidx / (D / 8), c8 = cidx % (D / 8);
-        *(u32x4*)(&k_lds[buf][row * KSTR + c8 * 8]) = kreg[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < VPT; ++r) {
-      const int u = tid + r * NT;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int dch = u % (D / 8), kg = u / (D / 8);
-        const int pos = (kg >> 2) * 16 + 4 * vt_group_pos(kg & 3);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = vreg[r][0][w], a1 = vreg[r][1][w], a2 = vreg[r][2][w], a3 = vreg[r][3][w];
-          // dim 2w: low halves; dim 2w+1: high halves; keys 0..3 packed along the row
-          const u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-          const u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-          *(u32x2*)(&vt_lds[buf][(dch * 8 + 2 * w) * VSTR + pos]) = lo;
-          *(u32x2*)(&vt_lds[buf][(dch * 8 + 2 * w + 1) * VSTR + pos]) = hi;
-        }
-      }
-    }
-  };
-
-  // ---- running statistics (base-2 units), per lane = per query, split over 2 lanes
-  float m_ref = kMaxInit;   // reference maximum the sums are relative to
-  float m_true = kMaxInit;  // true running maximum
-  float s1 = 0.0f, s2 = 0.0f;
+  // running statistics (base 2), per lane = per query; each row is split over 2 lanes
+  float m_ref = kMaxInit;   // the reference maximum the sums are relative to
+  float t_max = -INFINITY;  // true maximum of this lane's raw scores
+  float s1[4] = {0.f, 0.f, 0.f, 0.f};
+  float s2[4] = {0.f, 0.f, 0.f, 0.f};
   f32x16 o[DM];
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dm][e] = 0.0f;
 
-  auto compute_tile = [&](int buf, int kv0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto compute_tile = [&](const __bf16* kt, const __bf16* vt, int kv0) {
+    // ---- a3: S^T = K Q^T
     f32x16 s[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = *(const bf16x8*)(&k_lds[buf][(mb * 32 + col) * KSTR + ks * 16 + 8 * half]);
+        const bf16x8 a = *(const bf16x8*)(kt + k_off[ks] + mb * 32 * D);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
       }
-    }
-    if constexpr (MASK) {
+    // ---- mask on the diagonal / tail tiles only (in place)
+    if (kv0 + BN - 1 > kmax) {
+      const int lim = kmax - kv0 - 4 * half;  // key offset limit for this lane
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kv0 + mb * 32 + 8 * i + 4 * half + j;
-            if (key > kmax) s[mb][4 * i + j] = -INFINITY;
-          }
+          for (int j = 0; j < 4; ++j)
+            if (mb * 32 + 8 * i + j > lim) s[mb][4 * i + j] = -INFINITY;
     }
-    float tmax = -INFINITY;
+    // ---- a4: tile maximum; move the reference only when needed
+    float mx = s[0][0];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float cm = c * tmax;
-    m_true = fmaxf(m_true, cm);
-    if (__ballot(cm > m_ref + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_ref, cm);
+      for (int e = (mb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+    t_max = fmaxf(t_max, mx);
+    if (__ballot(c * mx > m_ref + kRescaleSlack) != 0) {
+      const float row_max = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_ref, c * row_max);
       const float alpha = fast_exp2(m_ref - m_new);
-      s1 *= alpha;
-      s2 *= alpha * alpha;  // squared correction factor
+      const float alpha2 = alpha * alpha;  // squared correction factor
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s1[u] *= alpha;
+        s2[u] *= alpha2;
+      }
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dm][e] *= alpha;
       m_ref = m_new;
     }
+    // ---- a5: p = exp2(c s - m), streamed sums, P -> bf16 in the B-operand order
     const float neg_m = -m_ref;
     bf16x8 pf[PS];
 #pragma unroll
@@ -214,44 +229,51 @@ __global__ __launch_bounds__(NW * 64) void polar_fwd_bf16_kernel(const FwdParams
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float pv = fast_exp2(fmaf(c, s[mb][4 * i + j], neg_m));
-          s1 += pv;
-          s2 = fmaf(pv, pv, s2);
+          s1[j] += pv;
+          s2[j] = fmaf(pv, pv, s2[j]);
           pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
         }
+    // ---- a6: O^T += V^T P^T
 #pragma unroll
-    for (int kst = 0; kst < PS; ++kst) {
+    for (int kst = 0; kst < PS; ++kst)
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
-        const bf16x8 a = *(const bf16x8*)(&vt_lds[buf][(dm * 32 + col) * VSTR + kst * 16 + 8 * half]);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt + v_off[0][dm] + kst * 16 * D));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt + v_off[1][dm] + kst * 16 * D));
+        const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
         o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kst], o[dm], 0, 0, 0);
       }
-    }
   };
 
-  // ---- main loop
-  load_tile(0);
-  store_tile(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int kv0 = t * BN;
-    if (!CAUSAL || kv0 <= wave_kmax) {
-      if (t >= first_mask_tile)
-        compute_tile(buf, kv0, std::true_type{});
-      else
-        compute_tile(buf, kv0, std::false_type{});
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) {
+      load_tile<D, BN, NW>(kb, (t + 1) * BN, Tk, k_buf1, wave, lane);
+      load_tile<D, BN, NW>(vb, (t + 1) * BN, Tk, v_buf1, wave, lane);
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    if (!CAUSAL || t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) {
+      load_tile<D, BN, NW>(kb, (t + 2) * BN, Tk, k_buf0, wave, lane);
+      load_tile<D, BN, NW>(vb, (t + 2) * BN, Tk, v_buf0, wave, lane);
+    }
+    if (!CAUSAL || (t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
     __syncthreads();
   }
 
-  // ---- epilogue: combine the two halves, form the channels [ATMA §2.1]
-  s1 += xor32(s1);
-  s2 += xor32(s2);
+  // ---- a7: combine the two halves of each row, form the channels [ATMA §2.1]
+  float S1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+  float S2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+  S1 += xor32(S1);
+  S2 += xor32(S2);
+  const float m_true = c * fmaxf(t_max, xor32(t_max));
   const float to_true = fast_exp2(m_ref - m_true);
-  const float S1 = s1 * to_true;
-  const float S2 = s2 * to_true * to_true;
+  S1 *= to_true;
+  S2 *= to_true * to_true;
   float nn = 0.0f;
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm)

@@ -21,11 +21,21 @@ using polar::FwdParams;
 using polar::HeadParams;
 using polar::MergeParams;
 
-// Prefill launch geometry (one configuration per dtype and head_dim).
-constexpr int kBf16Waves = 4;           // 128 query rows per workgroup
-constexpr int kBf16BlockN_d64 = 128;    // keys per LDS tile at head_dim 64
-constexpr int kBf16BlockN_d128 = 64;    // keys per LDS tile at head_dim 128
-constexpr int kF32Rows = 128;           // query rows per workgroup, fp32 path
+// Prefill launch geometry (one configuration per dtype and head_dim).  The macros only
+// exist so that tile sweeps can rebuild the library with other values.
+#ifndef POLAR_BF16_WAVES
+#define POLAR_BF16_WAVES 4
+#endif
+#ifndef POLAR_BF16_OCC_D64
+#define POLAR_BF16_OCC_D64 2
+#endif
+#ifndef POLAR_BF16_OCC_D128
+#define POLAR_BF16_OCC_D128 2
+#endif
+constexpr int kBf16Waves = POLAR_BF16_WAVES;      // query rows per workgroup = 32 x waves
+constexpr int kBf16Occ_d64 = POLAR_BF16_OCC_D64;  // waves per SIMD the registers must allow
+constexpr int kBf16Occ_d128 = POLAR_BF16_OCC_D128;
+constexpr int kF32Rows = 128;                         // query rows per workgroup, fp32 path
 // Decode launch geometry.
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeUnroll = 8;
@@ -108,12 +118,12 @@ template <int D, bool CAUSAL>
 polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
   const long long BH = (long long)pr->batch * pr->heads;
   if (pr->dtype == POLAR_BF16) {
-    constexpr int BN = D == 64 ? kBf16BlockN_d64 : kBf16BlockN_d128;
     constexpr int BM = kBf16Waves * 32;
     fp.n_qt = (pr->seq_q + BM - 1) / BM;
     const long long blocks = (long long)fp.n_qt * BH;
     if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, CAUSAL>, dim3((unsigned)blocks),
+    constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
+    return launch(polar::polar_fwd_bf16_kernel<D, kBf16Waves, OCC, CAUSAL>, dim3((unsigned)blocks),
                   dim3(kBf16Waves * 64), fp, stream);
   }
   fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;
