@@ -30,12 +30,20 @@
 //     the P V product; they are combined once, in the epilogue.
 #pragma once
 
+#ifndef POLAR_SCHED_HINTS
+#define POLAR_SCHED_HINTS 1
+#endif
+
+#include <type_traits>
+
 #include "polar_common.h"
 
 namespace polar {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 #define POLAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define POLAR_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
 
@@ -54,37 +62,50 @@ __device__ __forceinline__ int chunk_swizzle(int row) {
   }
 }
 
-// Issue the direct global->LDS loads of one BN x D bf16 tile whose first row is key
-// kv0.  Every wave-wide instruction fills 1 KiB of LDS (lane i -> bytes [16 i, 16 i + 16));
-// the lane chooses its global chunk so that the LDS image is the swizzled tile.  Rows
-// past the last key repeat the last key (their scores are masked).
+// Byte offset, inside a K or V tile, of the 16-byte global chunk this lane loads with
+// the wave's first tile-load instruction.  Every wave-wide load fills 1 KiB of LDS
+// (lane i -> bytes [16 i, 16 i + 16)); the lane picks its global chunk so that the LDS
+// image is the swizzled tile.  Instruction r of the wave (tile bytes
+// [(wave + NW r) KiB, +1 KiB)) reads NW KiB further on in the head's rows, where the
+// swizzle repeats, so the same offset serves every instruction and every tile.
+template <int D, int NW>
+__device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static_assert((NW * 64 / CPR) % 16 == 0, "the row advance per instruction must keep the swizzle");
+  const int idx = wave * 64 + lane;
+  const int row = idx / CPR;
+  const int lc = (idx % CPR) ^ chunk_swizzle<D>(row);
+  return (uint32_t)((row * D + lc * 8) * 2);
+}
+
+// Issue the buffer loads that bring the BN x D bf16 tile starting at key kv0 straight
+// into LDS.  Rows at or past the end of the head's keys lie outside the buffer range
+// and read as zero.
 template <int D, int BN, int NW>
-__device__ __forceinline__ void load_tile(const __bf16* src, int kv0, int Tk, __bf16* dst, int wave, int lane) {
-  constexpr int CPR = D / 8;
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int kv0, uint32_t voff, __bf16* dst,
+                                          int wave) {
   constexpr int INSTR = BN * D * 2 / 1024;
   static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
 #pragma unroll
   for (int r = 0; r < INSTR / NW; ++r) {
     const int i = wave + r * NW;
-    const int idx = i * 64 + lane;
-    const int row = idx / CPR;
-    const int lc = (idx % CPR) ^ chunk_swizzle<D>(row);
-    const int key = min(kv0 + row, Tk - 1);
-    __builtin_amdgcn_global_load_lds(POLAR_GLOBAL(src + (size_t)key * D + lc * 8), POLAR_LDS(dst + i * 512), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, POLAR_LDS(dst + i * 512), 16, voff,
+                                             (uint32_t)(kv0 * D * 2 + r * NW * 1024), 0, 0);
   }
 }
 
-template <int D, int NW, int OCC, bool CAUSAL>
+template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_fwd_bf16_kernel(
     const FwdParams p) {
-  constexpr int BN = 64;
-  constexpr int BM = NW * 32;
-  constexpr int MB = BN / 32;  // 32-key blocks per tile
-  constexpr int KS = D / 16;   // k-steps of Q K^T
-  constexpr int DM = D / 32;   // 32-wide d blocks of P V
-  constexpr int PS = BN / 16;  // k-steps of P V
+  static_assert(BN == 32 || BN == 64, "key tile");
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(NB == 1 || NB == 2, "query blocks per wave");
+  constexpr int QPW = 32 * NB;  // query rows per wave
+  constexpr int BM = NW * QPW;  // query rows per workgroup
+  constexpr int MB = BN / 32;   // 32-key blocks per tile
+  constexpr int KS = D / 16;    // k-steps of Q K^T
+  constexpr int DM = D / 32;    // 32-wide d blocks of P V
+  constexpr int PS = BN / 16;   // k-steps of P V
 
   __shared__ __attribute__((aligned(1024))) __bf16 k_buf0[BN * D];
   __shared__ __attribute__((aligned(1024))) __bf16 k_buf1[BN * D];
@@ -93,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -105,44 +126,61 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   const int Tq = p.Tq, Tk = p.Tk;
   const int off = Tk - Tq;
   const int q0 = qt * BM;
-  const int qrow = q0 + wave * 32 + col;
+  const int wq0 = q0 + wave * QPW;  // first query row of this wave
 
   const __bf16* qb = (const __bf16*)p.q + (size_t)bh * Tq * D;
-  const __bf16* kb = (const __bf16*)p.k + (size_t)(b * p.Hkv + hk) * Tk * D;
-  const __bf16* vb = (const __bf16*)p.v + (size_t)(b * p.Hkv + hk) * Tk * D;
+  const size_t kv_head = (size_t)(b * p.Hkv + hk) * Tk * D;
+  const uint32_t head_bytes = (uint32_t)((size_t)Tk * D * 2);
+  const __amdgpu_buffer_rsrc_t kb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)p.k + kv_head), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)p.v + kv_head), (short)0, head_bytes, 0x00020000);
+  const uint32_t voff = tile_lane_offset<D, NW>(wave, lane);
 
   const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
   const int ntiles = (kv_end + BN - 1) / BN;
-  const int wave_kmax = CAUSAL ? min(q0 + wave * 32 + 31 + off, Tk - 1) : Tk - 1;
+  // last key any row of the wave may see, and the smallest such limit over its rows
+  const int wave_kmax = CAUSAL ? min(wq0 + QPW - 1 + off, Tk - 1) : Tk - 1;
+  const int wave_kmin = CAUSAL ? min(wq0 + off, Tk - 1) : Tk - 1;
 
   // Start the first tile's loads before anything else.
-  load_tile<D, BN, NW>(kb, 0, Tk, k_buf0, wave, lane);
-  load_tile<D, BN, NW>(vb, 0, Tk, v_buf0, wave, lane);
+  load_tile<D, BN, NW>(kb, 0, voff, k_buf0, wave);
+  load_tile<D, BN, NW>(vb, 0, voff, v_buf0, wave);
 
+  // a1: per query block: row, visible count, temperature, base-2 logit scale, mask limit
   const int hpi = h * p.hp_stride;
-  const int n_vis = visible_keys(qrow, Tq, Tk, CAUSAL);
-  const float lam = length_temperature(p.hp.tau[hpi], n_vis);
-  const float c = lam * p.scale * kLog2e;
-  const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;  // last key this row may see
-
-  // Q^T fragments: lane holds query qrow, dims ks*16 + 8*half + [0, 8).
-  bf16x8 qf[KS];
+  int qrow[NB], n_vis[NB], kmax[NB];
+  float lam[NB], c[NB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (qrow < Tq) {
-      qf[ks] = *(const bf16x8*)(qb + (size_t)qrow * D + ks * 16 + 8 * half);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
-    }
+  for (int nb = 0; nb < NB; ++nb) {
+    qrow[nb] = wq0 + nb * 32 + col;
+    n_vis[nb] = visible_keys(qrow[nb], Tq, Tk, CAUSAL);
+    lam[nb] = length_temperature(p.hp.tau[hpi], n_vis[nb]);
+    c[nb] = lam[nb] * p.scale * kLog2e;
+    kmax[nb] = CAUSAL ? min(qrow[nb] + off, Tk - 1) : Tk - 1;
   }
 
-  // LDS element offsets of this lane's operand reads (same for both buffers).
-  // K (A operand of S^T): row mb*32 + col, logical chunk 2*ks + half.
-  const int k_sw = chunk_swizzle<D>(col);
-  int k_off[KS];
+  // Q^T fragments: lane holds query qrow[nb], dims ks*16 + 8*half + [0, 8).
+  bf16x8 qf[NB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * D + (((2 * ks + half) ^ k_sw) << 3);
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (qrow[nb] < Tq) {
+        qf[nb][ks] = *(const bf16x8*)(qb + (size_t)qrow[nb] * D + ks * 16 + 8 * half);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (__bf16)0.0f;
+      }
+    }
+
+  // LDS byte offsets of this lane's operand reads (same for both buffers).
+  // K (A operand of S^T): row mb*32 + col, logical chunk 2*ks + half, stored at chunk
+  // (2 ks + half) ^ sw = 2 (ks ^ (x >> 1)) + (x & 1) with x = half ^ sw, so the byte
+  // offset is k_base + ((32 ks) ^ k_xor).
+  const int k_x = half ^ chunk_swizzle<D>(col);
+  const uint32_t k_base = (uint32_t)(col * D * 2 + 16 * (k_x & 1));
+  const uint32_t k_xor = (uint32_t)(32 * (k_x >> 1));
   // V (A operand of O^T via transpose reads): in the 16-lane group g = lane / 16 the lane
   // points at key (4 * half + gi / 4) [+ 8 for the second read] and dims
   // dm*32 + 16*(g & 1) + 4*(gi & 3) .. + 3.
@@ -160,80 +198,96 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     }
   }
 
-  // running statistics (base 2), per lane = per query; each row is split over 2 lanes
-  float m_ref = kMaxInit;   // the reference maximum the sums are relative to
-  float t_max = -INFINITY;  // true maximum of this lane's raw scores
-  float s1[4] = {0.f, 0.f, 0.f, 0.f};
-  float s2[4] = {0.f, 0.f, 0.f, 0.f};
-  f32x16 o[DM];
+  // running statistics (base 2), per lane and query block; each row is split over the
+  // two lanes l and l ^ 32
+  float m_ref[NB], t_max[NB], s1[NB][2], s2[NB][2];
+  f32x16 o[NB][DM];
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm)
+  for (int nb = 0; nb < NB; ++nb) {
+    m_ref[nb] = kMaxInit;   // the reference maximum the sums are relative to
+    t_max[nb] = -INFINITY;  // true maximum of this lane's raw scores
+    s1[nb][0] = s1[nb][1] = s2[nb][0] = s2[nb][1] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[dm][e] = 0.0f;
+    for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[nb][dm][e] = 0.0f;
+  }
 
   auto compute_tile = [&](const __bf16* kt, const __bf16* vt, int kv0) {
-    // ---- a3: S^T = K Q^T
-    f32x16 s[MB];
+    // ---- a3: S^T = K Q^T; each K fragment feeds the NB query blocks
+    f32x16 s[NB][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[nb][mb][e] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = *(const bf16x8*)(kt + k_off[ks] + mb * 32 * D);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+        const bf16x8 a = *(const bf16x8*)((const char*)kt + (k_base + ((32u * ks) ^ k_xor)) + mb * 32 * D * 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], s[nb][mb], 0, 0, 0);
       }
-    // ---- mask on the diagonal / tail tiles only (in place)
-    if (kv0 + BN - 1 > kmax) {
-      const int lim = kmax - kv0 - 4 * half;  // key offset limit for this lane
+    bf16x8 pf[NB][PS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // ---- mask on the diagonal / tail tiles only (in place)
+      if (kv0 + BN - 1 > wave_kmin) {
+        const int lim = kmax[nb] - kv0 - 4 * half;  // key offset limit for this lane
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (mb * 32 + 8 * i + j > lim) s[nb][mb][4 * i + j] = -INFINITY;
+      }
+      // ---- a4: tile maximum; move the reference only when a score exceeds it by 2^8
+      float mx = s[nb][0][0];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = (mb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][mb][e]);
+      t_max[nb] = fmaxf(t_max[nb], mx);
+      if (__ballot(c[nb] * mx > m_ref[nb] + kRescaleSlack) != 0) {
+        const float row_max = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_ref[nb], c[nb] * row_max);
+        const float alpha = fast_exp2(m_ref[nb] - m_new);
+        const float alpha2 = alpha * alpha;  // squared correction factor
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          s1[nb][u] *= alpha;
+          s2[nb][u] *= alpha2;
+        }
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[nb][dm][e] *= alpha;
+        m_ref[nb] = m_new;
+      }
+      // ---- a5: p = exp2(c s - m) rounded to bf16 in the B-operand order; sum p and
+      // sum p^2 are taken from the same bf16 weights, two at a time (exact products,
+      // fp32 sums)
+      const float neg_m = -m_ref[nb];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (mb * 32 + 8 * i + j > lim) s[mb][4 * i + j] = -INFINITY;
+          for (int j = 0; j < 4; j += 2) {
+            bf16x2 pp;
+            pp[0] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j], neg_m));
+            pp[1] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j + 1], neg_m));
+            s1[nb][j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, s1[nb][j >> 1], false);
+            s2[nb][j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, s2[nb][j >> 1], false);
+            pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
+            pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = pp[1];
+          }
     }
-    // ---- a4: tile maximum; move the reference only when needed
-    float mx = s[0][0];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int e = (mb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    t_max = fmaxf(t_max, mx);
-    if (__ballot(c * mx > m_ref + kRescaleSlack) != 0) {
-      const float row_max = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_ref, c * row_max);
-      const float alpha = fast_exp2(m_ref - m_new);
-      const float alpha2 = alpha * alpha;  // squared correction factor
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        s1[u] *= alpha;
-        s2[u] *= alpha2;
-      }
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dm][e] *= alpha;
-      m_ref = m_new;
-    }
-    // ---- a5: p = exp2(c s - m), streamed sums, P -> bf16 in the B-operand order
-    const float neg_m = -m_ref;
-    bf16x8 pf[PS];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pv = fast_exp2(fmaf(c, s[mb][4 * i + j], neg_m));
-          s1[j] += pv;
-          s2[j] = fmaf(pv, pv, s2[j]);
-          pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
-        }
-    // ---- a6: O^T += V^T P^T
+    // ---- a6: O^T += V^T P^T; each V fragment feeds the NB query blocks
 #pragma unroll
     for (int kst = 0; kst < PS; ++kst)
 #pragma unroll
@@ -244,66 +298,72 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             (__attribute__((address_space(3))) s16x4*)(vt + v_off[1][dm] + kst * 16 * D));
         const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 a = __builtin_bit_cast(bf16x8, both);
-        o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kst], o[dm], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          o[nb][dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[nb][kst], o[nb][dm], 0, 0, 0);
       }
   };
 
+  // ---- main loop: tile t is read from one buffer pair while tile t+1 loads into the other
   __syncthreads();
   for (int t = 0; t < ntiles; t += 2) {
     if (t + 1 < ntiles) {
-      load_tile<D, BN, NW>(kb, (t + 1) * BN, Tk, k_buf1, wave, lane);
-      load_tile<D, BN, NW>(vb, (t + 1) * BN, Tk, v_buf1, wave, lane);
+      load_tile<D, BN, NW>(kb, (t + 1) * BN, voff, k_buf1, wave);
+      load_tile<D, BN, NW>(vb, (t + 1) * BN, voff, v_buf1, wave);
     }
-    if (!CAUSAL || t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
+    if (t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
     __syncthreads();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) {
-      load_tile<D, BN, NW>(kb, (t + 2) * BN, Tk, k_buf0, wave, lane);
-      load_tile<D, BN, NW>(vb, (t + 2) * BN, Tk, v_buf0, wave, lane);
+      load_tile<D, BN, NW>(kb, (t + 2) * BN, voff, k_buf0, wave);
+      load_tile<D, BN, NW>(vb, (t + 2) * BN, voff, v_buf0, wave);
     }
-    if (!CAUSAL || (t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
+    if ((t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
     __syncthreads();
   }
 
   // ---- a7: combine the two halves of each row, form the channels [ATMA §2.1]
-  float S1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
-  float S2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
-  S1 += xor32(S1);
-  S2 += xor32(S2);
-  const float m_true = c * fmaxf(t_max, xor32(t_max));
-  const float to_true = fast_exp2(m_ref - m_true);
-  S1 *= to_true;
-  S2 *= to_true * to_true;
-  float nn = 0.0f;
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) nn = fmaf(o[dm][e], o[dm][e], nn);
-  nn += xor32(nn);
-  const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
-  if (qrow < Tq) {
-    const size_t row = (size_t)bh * Tq + qrow;
-    float* drow = p.dir + row * D;
+  for (int nb = 0; nb < NB; ++nb) {
+    float S1 = s1[nb][0] + s1[nb][1];
+    float S2 = s2[nb][0] + s2[nb][1];
+    S1 += xor32(S1);
+    S2 += xor32(S2);
+    const float m_true = c[nb] * fmaxf(t_max[nb], xor32(t_max[nb]));
+    const float to_true = fast_exp2(m_ref[nb] - m_true);
+    S1 *= to_true;
+    S2 *= to_true * to_true;
+    float nn = 0.0f;
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 val = {o[dm][4 * i] * inv, o[dm][4 * i + 1] * inv, o[dm][4 * i + 2] * inv,
-                           o[dm][4 * i + 3] * inv};
-        *(f32x4*)(drow + dm * 32 + 8 * i + 4 * half) = val;
-      }
-    if (half == 0) {
-      const float m_nat = m_true * kLn2;
-      float neff, conf, count;
-      magnitude_channel(m_nat, S1, S2, n_vis, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf,
-                        count);
-      p.neff[row] = neff;
-      if (p.conf) p.conf[row] = conf;
-      if (p.count) p.count[row] = count;
-      if (p.stats) {
-        p.stats[row * 3 + 0] = m_nat;
-        p.stats[row * 3 + 1] = S1;
-        p.stats[row * 3 + 2] = S2;
+      for (int e = 0; e < 16; ++e) nn = fmaf(o[nb][dm][e], o[nb][dm][e], nn);
+    nn += xor32(nn);
+    const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+    if (qrow[nb] < Tq) {
+      const size_t row = (size_t)bh * Tq + qrow[nb];
+      float* drow = p.dir + row * D;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 val = {o[nb][dm][4 * i] * inv, o[nb][dm][4 * i + 1] * inv, o[nb][dm][4 * i + 2] * inv,
+                             o[nb][dm][4 * i + 3] * inv};
+          *(f32x4*)(drow + dm * 32 + 8 * i + 4 * half) = val;
+        }
+      if (half == 0) {
+        const float m_nat = m_true * kLn2;
+        float neff, conf, count;
+        magnitude_channel(m_nat, S1, S2, n_vis[nb], lam[nb], p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff,
+                          conf, count);
+        p.neff[row] = neff;
+        if (p.conf) p.conf[row] = conf;
+        if (p.count) p.count[row] = count;
+        if (p.stats) {
+          p.stats[row * 3 + 0] = m_nat;
+          p.stats[row * 3 + 1] = S1;
+          p.stats[row * 3 + 2] = S2;
+        }
       }
     }
   }

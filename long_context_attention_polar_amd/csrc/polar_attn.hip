@@ -26,6 +26,18 @@ using polar::MergeParams;
 #ifndef POLAR_BF16_WAVES
 #define POLAR_BF16_WAVES 4
 #endif
+#ifndef POLAR_BF16_BN_D64
+#define POLAR_BF16_BN_D64 64
+#endif
+#ifndef POLAR_BF16_BN_D128
+#define POLAR_BF16_BN_D128 64
+#endif
+#ifndef POLAR_BF16_NB_D64
+#define POLAR_BF16_NB_D64 2
+#endif
+#ifndef POLAR_BF16_NB_D128
+#define POLAR_BF16_NB_D128 1
+#endif
 #ifndef POLAR_BF16_OCC_D64
 #define POLAR_BF16_OCC_D64 2
 #endif
@@ -33,6 +45,10 @@ using polar::MergeParams;
 #define POLAR_BF16_OCC_D128 2
 #endif
 constexpr int kBf16Waves = POLAR_BF16_WAVES;      // query rows per workgroup = 32 x waves
+constexpr int kBf16Bn_d64 = POLAR_BF16_BN_D64;    // keys per LDS tile
+constexpr int kBf16Bn_d128 = POLAR_BF16_BN_D128;
+constexpr int kBf16Nb_d64 = POLAR_BF16_NB_D64;    // 32-row query blocks per wave
+constexpr int kBf16Nb_d128 = POLAR_BF16_NB_D128;
 constexpr int kBf16Occ_d64 = POLAR_BF16_OCC_D64;  // waves per SIMD the registers must allow
 constexpr int kBf16Occ_d128 = POLAR_BF16_OCC_D128;
 constexpr int kF32Rows = 128;                         // query rows per workgroup, fp32 path
@@ -118,12 +134,14 @@ template <int D, bool CAUSAL>
 polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
   const long long BH = (long long)pr->batch * pr->heads;
   if (pr->dtype == POLAR_BF16) {
-    constexpr int BM = kBf16Waves * 32;
+    constexpr int NB = D == 64 ? kBf16Nb_d64 : kBf16Nb_d128;
+    constexpr int BM = kBf16Waves * 32 * NB;
     fp.n_qt = (pr->seq_q + BM - 1) / BM;
     const long long blocks = (long long)fp.n_qt * BH;
     if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
     constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
-    return launch(polar::polar_fwd_bf16_kernel<D, kBf16Waves, OCC, CAUSAL>, dim3((unsigned)blocks),
+    constexpr int BN = D == 64 ? kBf16Bn_d64 : kBf16Bn_d128;
+    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL>, dim3((unsigned)blocks),
                   dim3(kBf16Waves * 64), fp, stream);
   }
   fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;
