@@ -6,28 +6,32 @@
 // never stored.
 //
 // Work decomposition
-//   * A workgroup of NW waves owns BM = 32 * NW query rows of one (b, h); each wave
-//     owns 32 rows.  Keys stream through LDS in tiles of BN = 64 rows, double-buffered,
-//     with direct global->LDS loads (no registers, no LDS store instructions): the loads
-//     of tile t+1 are in flight while tile t is computed, and one barrier per tile
-//     publishes them.  K and V stay row-major in LDS; the 16-byte chunks of a row are
-//     XOR-swizzled so both read patterns below are free of bank conflicts.
+//   * A workgroup of NW waves owns BM = 32 * NB * NW query rows of one (b, h); each wave
+//     owns NB blocks of 32 rows (two at d = 64, so every K and V operand read from LDS
+//     feeds two MFMAs).  Keys stream through LDS in tiles of BN = 64 rows,
+//     double-buffered, with direct global->LDS buffer loads (no registers, no LDS store
+//     instructions): the loads of tile t+1 are in flight while tile t is computed, and
+//     one barrier per tile publishes them.  Rows past the end of the keys fall outside
+//     the buffer range and read as zero.  K and V stay row-major in LDS; the 16-byte
+//     chunks of a row are XOR-swizzled so both read patterns below are free of bank
+//     conflicts.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (A = K rows from LDS, B = the wave's Q^T fragment held in registers).  In the
 //     32x32 accumulator layout lane l holds query (l % 32) and 16 of every 32 keys, so a
 //     row's statistics are per-lane scalars split over two lanes (l, l ^ 32).
-//   * The output is accumulated transposed, O^T += V^T P^T.  The probabilities are used
-//     in place as the B operand once the keys of each 16-key step are taken in the
-//     order 0-3, 8-11, 4-7, 12-15; the matching V^T operand comes straight from the
-//     row-major V tile through two ds_read_b64_tr_b16 transpose reads, each delivering
-//     four consecutive keys of one dimension to a lane.
-//   * The reference maximum moves only when a score exceeds it by more than 2^8 (base 2),
-//     decided for the whole wave with one ballot; only then are the two halves of a row
-//     exchanged and sum p, sum p^2 (by alpha^2) and acc rescaled.  The true maximum is
-//     tracked on the side for the reported statistics.
-//   * sum p and sum p^2 are fp32 per-lane partial sums (four of each, to keep the
-//     dependency chains short), taken from the fp32 p before it is rounded to bf16 for
-//     the P V product; they are combined once, in the epilogue.
+//   * The output is accumulated transposed, O^T += V^T P^T.  The weights are used in
+//     place as the B operand once the keys of each 16-key step are taken in the order
+//     0-3, 8-11, 4-7, 12-15; the matching V^T operand comes straight from the row-major
+//     V tile through two ds_read_b64_tr_b16 transpose reads, each delivering four
+//     consecutive keys of one dimension to a lane.
+//   * A tile is two 32-key blocks.  The reference maximum moves only when a score
+//     exceeds it by more than 2^8 (base 2), decided for the whole wave with one ballot
+//     per block; only then are the two halves of a row exchanged and sum p, sum p^2 (by
+//     alpha^2) and acc rescaled.  The true maximum is tracked on the side for the
+//     reported statistics.
+//   * sum p and sum p^2 are taken from the same bf16-rounded weights that enter P V, two
+//     at a time with v_dot2_f32_bf16 (exact products, fp32 sums), as per-lane partial
+//     sums combined once in the epilogue.
 #pragma once
 
 #ifndef POLAR_SCHED_HINTS
@@ -89,8 +93,9 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int kv0, 
 #pragma unroll
   for (int r = 0; r < INSTR / NW; ++r) {
     const int i = wave + r * NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, POLAR_LDS(dst + i * 512), 16, voff,
-                                             (uint32_t)(kv0 * D * 2 + r * NW * 1024), 0, 0);
+    // the whole byte offset sits in the VGPR operand, which the range check covers
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, POLAR_LDS(dst + i * 512), 16,
+                                             voff + (uint32_t)(kv0 * D * 2 + r * NW * 1024), 0, 0, 0);
   }
 }
 
