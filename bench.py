@@ -7,7 +7,10 @@ already resident in HBM:
   * fused prefill forward, bf16, B=1 H=16 T=65536 d=64, causal, tau_h = 0.02 h
     (the longest context the ATMA summary evaluates, §3);
   * split-KV decode + merge, bf16, batch 64, H=8, d=128, one query against a
-    65536-token KV cache.
+    65536-token KV cache;
+  * grouped split-KV decode + merge over a paged cache, bf16, batch 64, 32 query heads
+    over 8 KV heads, d=128, 65536 keys per sequence in shuffled 16-row blocks (reported
+    beside the headline, not part of it).
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -31,6 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
 DECODE = "bf16_decode_b64_h8_tk65536_d128"
+PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -48,6 +52,7 @@ def prefill_flops(w):
 
 
 def decode_bytes(w):
+    """Algorithmic bytes: K and V once per (sequence, KV head), q and the outputs."""
     kv = 2 * w.B * w.Hkv * w.Tk * w.d * 2
     q = w.B * w.H * w.d * 2
     outs = w.B * w.H * (w.d + 3) * 4   # direction, n_eff, confidence, count... (+ stats not requested)
@@ -153,6 +158,15 @@ def main():
     kwd = dict(len_temp=wd.len_temp(), null_bias=wd.null_bias(), count_scale=wd.count_scale())
     parts.append(dict(name=DECODE, w=wd, kind="decode", bytes=decode_bytes(wd),
                       run=lambda: pa.decode(qd, kd, vd, workspace=ws, out=outd, **kwd)))
+    wp = pin.WORKLOADS[PAGED]
+    qp, kpool, vpool, table, lens = pin.paged_decode_inputs(wp, dev)
+    probp = pa.Problem(wp.B, wp.H, wp.Hkv, 1, wp.Tk, wp.d, False, pa.POLAR_BF16)
+    need = pa.decode_paged_workspace_bytes(probp, pa.paged_kv(kpool, vpool, table, lens))
+    wsp = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    outp = pa.allocate_outputs(wp.B, wp.H, 1, wp.d, dev)
+    kwp = dict(seq_k=wp.Tk, len_temp=wp.len_temp(), null_bias=wp.null_bias(), count_scale=wp.count_scale())
+    parts.append(dict(name=PAGED, w=wp, kind="decode", bytes=decode_bytes(wp), headline=False,
+                      run=lambda: pa.decode_paged(qp, kpool, vpool, table, lens, workspace=wsp, out=outp, **kwp)))
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
@@ -189,7 +203,7 @@ def main():
             entry["gbs"] = p["bytes"] / (avg * 1e-3) / 1e9
             entry["frac_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS
             entry["bytes_per_launch"] = p["bytes"]
-            entry["splits"] = splits
+            entry["splits"] = splits if p["name"] == DECODE else None
         res[p["name"]] = entry
     assert torch.isfinite(outd["direction"]).all()  # a sanity check; parity is in the tests
 
@@ -215,6 +229,9 @@ def main():
                    "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
         "roofline": roofline,
         "decode": decode_roof,
+        "paged_gqa_decode": {"bound": "hbm", "achieved": res[PAGED]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": res[PAGED]["frac_hbm_peak"], "ms": res[PAGED]["ms_avg"],
+                             "note": "32 query heads share 8 KV heads; K and V are read once per group"},
         "parts": res,
         "source_digest": digest,
     }

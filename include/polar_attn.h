@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 1
+#define POLAR_ABI_VERSION 2
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -126,10 +126,52 @@ size_t polar_attn_decode_workspace_bytes(const polar_problem* problem, int32_t n
  * sequence) and bf16.  The cache of seq_k keys is cut into S contiguous splits; one
  * kernel writes the statistics (m, S1, S2, acc) of every split into `workspace` (layout
  * as for polar_attn_merge), and a second kernel on the same stream merges them with
- * the global visible count n = seq_k.  1 <= num_splits <= seq_k, or 0 for automatic. */
+ * the global visible count n = seq_k.  1 <= num_splits <= seq_k, or 0 for automatic.
+ * When heads > kv_heads, a workgroup serves up to 8 query heads of a group and reads
+ * each K and V row once for all of them. */
 polar_status polar_attn_decode(const polar_problem* problem, const void* q, const void* k_cache,
                                const void* v_cache, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, const polar_outputs* out, void* stream);
+
+/* Paged KV cache for polar_attn_decode_paged.  The keys of sequence b are stored in
+ * blocks of block_size rows: block_table[b * max_blocks + j] is the pool block holding
+ * keys [j * block_size, (j + 1) * block_size) of that sequence.  k_pool and v_pool are
+ * DEVICE [num_blocks, block_size, kv_heads, head_dim] bf16, contiguous, 16-byte
+ * aligned.  block_table is DEVICE int32 [batch, max_blocks]; seq_lens is DEVICE int32
+ * [batch], the number of cached keys of each sequence.  Both are read by the kernels
+ * only (the call never waits for them): a length outside [0, problem->seq_k] is clamped
+ * into it, and a table entry outside [0, num_blocks) is never dereferenced -- its keys
+ * are skipped, and the results of that sequence are then unspecified.  A sequence with
+ * no keys gets a zero direction and zero n_eff, confidence and count. */
+typedef struct polar_paged_kv {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t num_blocks;         /* >= 1                                                       */
+  int32_t block_size;         /* a power of two, 1 .. 1024                                  */
+  int32_t max_blocks;         /* table columns; max_blocks * block_size >= problem->seq_k   */
+} polar_paged_kv;
+
+/* Split count and workspace bytes polar_attn_decode_paged uses for `num_splits`
+ * (0 = automatic); 0 when the call is invalid. */
+int32_t polar_attn_decode_paged_num_splits(const polar_problem* problem, const polar_paged_kv* kv,
+                                           int32_t num_splits);
+size_t polar_attn_decode_paged_workspace_bytes(const polar_problem* problem, const polar_paged_kv* kv,
+                                               int32_t num_splits);
+
+/* Grouped split-KV decode over a paged cache [ATMA §2.2, decode kernel; grouped-query
+ * attention reads each KV row once per group].  Requires seq_q == 1 and bf16; q is
+ * DEVICE [batch, heads, head_dim].  problem->seq_k is the largest sequence length the
+ * call may see (it sizes the splits); causal is ignored: each query sees every cached
+ * key of its sequence, and its visible count n is that sequence's length.  One
+ * workgroup serves a (sequence, KV head, split) and up to 8 query heads of the group,
+ * loading each K and V row once for all of them.  Writes the same per-split partials
+ * as polar_attn_decode into `workspace` ([batch, heads, S, head_dim + 3] fp32) and then
+ * merges them on the same stream. */
+polar_status polar_attn_decode_paged(const polar_problem* problem, const void* q, const polar_paged_kv* kv,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     const polar_outputs* out, void* stream);
 
 /* Merge of split statistics [ATMA §2.2: streaming accumulators with squared correction
  * factors].  partials: DEVICE [B, heads, seq_q, num_splits, head_dim + 3] fp32, each row

@@ -43,6 +43,12 @@ class PolarOutputs(ctypes.Structure):
                 ("count", ctypes.c_void_p), ("stats", ctypes.c_void_p)]
 
 
+class PolarPagedKV(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32)]
+
+
 class PolarError(RuntimeError):
     def __init__(self, status: int, lib_message: str):
         self.status = status
@@ -77,6 +83,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_decode_num_splits.restype = ctypes.c_int32
     lib.polar_attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.polar_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    K = ctypes.POINTER(PolarPagedKV)
+    lib.polar_attn_decode_paged.argtypes = [P, vp, K, ctypes.c_int32, vp, ctypes.c_size_t, O, vp]
+    lib.polar_attn_decode_paged.restype = ctypes.c_int
+    lib.polar_attn_decode_paged_num_splits.argtypes = [P, K, ctypes.c_int32]
+    lib.polar_attn_decode_paged_num_splits.restype = ctypes.c_int32
+    lib.polar_attn_decode_paged_workspace_bytes.argtypes = [P, K, ctypes.c_int32]
+    lib.polar_attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
     lib.polar_status_string.argtypes = [ctypes.c_int]
     lib.polar_status_string.restype = ctypes.c_char_p
     lib.polar_abi_version.argtypes = []
@@ -242,9 +255,72 @@ def decode(q, k_cache, v_cache, *, num_splits=0, len_temp=None, null_bias=None, 
                                  _stream(dev)))
     out["splits"] = splits
     if splits > 0:
-        n = prob.batch * prob.heads * prob.seq_q * splits * (prob.head_dim + 3)
-        out["partials"] = workspace[:n * 4].view(torch.float32).view(prob.batch, prob.heads, prob.seq_q, splits,
-                                                                    prob.head_dim + 3)
+        out["partials"] = _partials_view(workspace, prob, splits)
+    return out
+
+
+def _partials_view(workspace, prob, splits):
+    n = prob.batch * prob.heads * prob.seq_q * splits * (prob.head_dim + 3)
+    return workspace[:n * 4].view(torch.float32).view(prob.batch, prob.heads, prob.seq_q, splits, prob.head_dim + 3)
+
+
+def paged_kv(k_pool, v_pool, block_table, seq_lens):
+    """Describe a paged cache: pools [num_blocks, block_size, Hkv, d] bf16, block_table
+    [B, max_blocks] int32 and seq_lens [B] int32, all on one GPU."""
+    dev = k_pool.device
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table), ("seq_lens", seq_lens)):
+        _check_tensor(name, t, dev)
+    if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
+        raise ValueError("k_pool and v_pool must both be [num_blocks, block_size, kv_heads, head_dim]")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or seq_lens.dim() != 1 or seq_lens.shape[0] != block_table.shape[0]:
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    nb, bs = k_pool.shape[0], k_pool.shape[1]
+    return PolarPagedKV(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), nb, bs, block_table.shape[1])
+
+
+def decode_paged_workspace_bytes(prob: Problem, kv: PolarPagedKV, num_splits: int = 0) -> int:
+    pr, keep = prob.to_c()
+    return int(load_library().polar_attn_decode_paged_workspace_bytes(ctypes.byref(pr), ctypes.byref(kv),
+                                                                      num_splits))
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, seq_k=None, num_splits=0, len_temp=None,
+                 null_bias=None, count_scale=None, softmax_scale=None, workspace=None, out=None, stats=False):
+    """Grouped split-KV decode over a paged cache (polar_attn_decode_paged).
+
+    q [B,H,1,d] bf16; pools [num_blocks, block_size, Hkv, d] bf16; block_table [B, max_blocks]
+    and seq_lens [B] int32.  seq_k: the largest sequence length (default: the table's
+    capacity, max_blocks * block_size).  Returns the same dict as decode()."""
+    dev = q.device
+    _check_tensor("q", q, dev)
+    kv = paged_kv(k_pool, v_pool, block_table, seq_lens)
+    B, H, Tq, d = q.shape
+    Hkv = k_pool.shape[2]
+    if k_pool.shape[3] != d or block_table.shape[0] != B:
+        raise ValueError("q, the pools and the block table disagree")
+    if seq_k is None:
+        seq_k = kv.max_blocks * kv.block_size
+    prob = Problem(B, H, Hkv, Tq, int(seq_k), d, False, _dtype_code(q), float(softmax_scale or 0.0),
+                   None if len_temp is None else list(len_temp),
+                   None if null_bias is None else list(null_bias),
+                   None if count_scale is None else list(count_scale))
+    lib = load_library()
+    pr, keep = prob.to_c()
+    splits = int(lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), num_splits))
+    need = int(lib.polar_attn_decode_paged_workspace_bytes(ctypes.byref(pr), ctypes.byref(kv), num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = allocate_outputs(B, H, Tq, d, dev, stats=stats)
+    oc = _outputs_c(out)
+    _check(lib.polar_attn_decode_paged(ctypes.byref(pr), _ptr(q), ctypes.byref(kv), num_splits, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), ctypes.byref(oc),
+                                       _stream(dev)))
+    out["splits"] = splits
+    if splits > 0:
+        out["partials"] = _partials_view(workspace, prob, splits)
     return out
 
 
@@ -269,6 +345,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["fwd", "decode", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["fwd", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

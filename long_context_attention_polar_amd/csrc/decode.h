@@ -203,10 +203,13 @@ __global__ __launch_bounds__(64) void polar_merge_kernel(const MergeParams p) {
   for (int e = 0; e < DPL; ++e) p.dir[row * D + lane + 64 * e] = acc[e] * inv;
   if (lane == 0) {
     const int hpi = h * p.hp_stride;
-    const int n = visible_keys(i, p.Tq, p.Tk, p.causal != 0);
-    const float lam = length_temperature(p.hp.tau[hpi], n);
-    float neff, conf, count;
-    magnitude_channel(M, S1, S2, n, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf, count);
+    int n = visible_keys(i, p.Tq, p.Tk, p.causal != 0);
+    if (p.lens) n = min(max(p.lens[row / ((size_t)p.H * p.Tq)], 0), p.Tk);
+    float neff = 0.0f, conf = 0.0f, count = 0.0f;
+    if (n > 0 && M > -INFINITY) {
+      const float lam = length_temperature(p.hp.tau[hpi], n);
+      magnitude_channel(M, S1, S2, n, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf, count);
+    }  // a row that saw no key: direction 0 and all channels 0
     p.neff[row] = neff;
     if (p.conf) p.conf[row] = conf;
     if (p.count) p.count[row] = count;

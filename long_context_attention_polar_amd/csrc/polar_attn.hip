@@ -10,6 +10,7 @@
 
 #include "../../include/polar_attn.h"
 #include "decode.h"
+#include "decode_group.h"
 #include "fwd_bf16.h"
 #include "fwd_f32.h"
 #include "polar_common.h"
@@ -150,9 +151,21 @@ polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
   return launch(polar::polar_fwd_f32_kernel<D, CAUSAL>, dim3((unsigned)blocks), dim3(kF32Rows), fp, stream);
 }
 
+// Query heads one grouped-decode workgroup serves: the largest of 8, 4, 2, 1 that divides
+// the group size heads / kv_heads.
+int group_chunk(const polar_problem* pr) {
+  const int g = pr->heads / pr->kv_heads;
+  for (int c = 8; c > 1; c >>= 1)
+    if (g % c == 0) return c;
+  return 1;
+}
+
 int auto_splits(const polar_problem* pr) {
   // Aim for about 4096 split workgroups (16 per CU) with at least 256 keys per split.
-  const long long rows = (long long)pr->batch * pr->heads;
+  // A workgroup serves one query head, or a chunk of a query-head group when heads share
+  // a KV head.
+  const long long rows = (long long)pr->batch * (pr->heads / group_chunk(pr));
+  if (rows <= 0) return 1;  // no rows: nothing is launched
   long long s = (4096 + rows - 1) / rows;
   const long long max_by_len = (pr->seq_k + 255) / 256;
   if (s > max_by_len) s = max_by_len;
@@ -175,11 +188,114 @@ size_t partial_bytes(const polar_problem* pr, int splits) {
   return (size_t)pr->batch * pr->heads * pr->seq_q * splits * (pr->head_dim + 3) * sizeof(float);
 }
 
+// Checks of a paged decode call that need no device memory.
+polar_status check_paged(const polar_problem* pr, const polar_paged_kv* kv, int32_t num_splits, int& splits) {
+  if (!kv) return POLAR_ERR_NULL_ARG;
+  polar_problem flat = *pr;
+  flat.causal = 0;  // the query sees every cached key of its sequence
+  const polar_status st = check_decode(&flat, 0, splits);
+  if (st != POLAR_OK) return st;
+  const int bs = kv->block_size;
+  if (bs < 1 || bs > 1024 || (bs & (bs - 1)) != 0) return POLAR_ERR_BAD_SHAPE;
+  if (kv->num_blocks < 1 || kv->max_blocks < 1) return POLAR_ERR_BAD_SHAPE;
+  if ((long long)kv->max_blocks * bs < pr->seq_k) return POLAR_ERR_BAD_SHAPE;
+  if (num_splits < 0 || num_splits > pr->seq_k) return POLAR_ERR_BAD_SHAPE;
+  splits = num_splits == 0 ? auto_splits(pr) : num_splits;
+  return POLAR_OK;
+}
+
+template <int D, bool PAGED>
+polar_status launch_group(int chunk, polar::GroupDecodeParams& gp, dim3 grid, void* stream) {
+  constexpr int NW = kDecodeWaves;
+  switch (chunk) {
+    case 1:
+      return launch(polar::polar_decode_group_kernel<D, 1, NW, 8, PAGED>, grid, dim3(NW * 64), gp, stream);
+    case 2:
+      return launch(polar::polar_decode_group_kernel<D, 2, NW, 4, PAGED>, grid, dim3(NW * 64), gp, stream);
+    case 4:
+      return launch(polar::polar_decode_group_kernel<D, 4, NW, 2, PAGED>, grid, dim3(NW * 64), gp, stream);
+    default:
+      return launch(polar::polar_decode_group_kernel<D, 8, NW, 2, PAGED>, grid, dim3(NW * 64), gp, stream);
+  }
+}
+
+// Grouped split kernel over a contiguous (kv == NULL) or paged cache; fills gp's common
+// fields.  The caller has validated everything.
+polar_status launch_grouped_splits(const polar_problem* pr, const polar_paged_kv* kv, const void* q,
+                                   const void* k, const void* v, int splits, void* workspace, void* stream) {
+  polar::GroupDecodeParams gp;
+  std::memset(&gp, 0, sizeof(gp));
+  int floor_on = 0;
+  const polar_status st = head_params(pr, gp.hp, gp.hp_stride, floor_on, gp.scale);
+  if (st != POLAR_OK) return st;
+  const int chunk = group_chunk(pr);
+  gp.q = q;
+  gp.k = k;
+  gp.v = v;
+  gp.part = (float*)workspace;
+  gp.B = pr->batch;
+  gp.H = pr->heads;
+  gp.Hkv = pr->kv_heads;
+  gp.Tk = pr->seq_k;
+  gp.S = splits;
+  gp.split_len = (pr->seq_k + splits - 1) / splits;
+  gp.chunks = (pr->heads / pr->kv_heads) / chunk;
+  if (kv) {
+    gp.table = kv->block_table;
+    gp.lens = kv->seq_lens;
+    gp.num_blocks = kv->num_blocks;
+    gp.max_blocks = kv->max_blocks;
+    int l2 = 0;
+    while ((1 << l2) < kv->block_size) ++l2;
+    gp.bs_log2 = l2;
+  }
+  const long long gy = (long long)pr->kv_heads * gp.chunks;
+  if (gy > 65535 || pr->batch > 65535) return POLAR_ERR_UNSUPPORTED;
+  const dim3 grid(splits, (unsigned)gy, pr->batch);
+  if (pr->head_dim == 64)
+    return kv ? launch_group<64, true>(chunk, gp, grid, stream) : launch_group<64, false>(chunk, gp, grid, stream);
+  return kv ? launch_group<128, true>(chunk, gp, grid, stream) : launch_group<128, false>(chunk, gp, grid, stream);
+}
+
 template <int D>
 polar_status launch_merge(const polar_problem* pr, MergeParams& mp, void* stream) {
   const long long rows = (long long)pr->batch * pr->heads * pr->seq_q;
   if (rows > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
   return launch(polar::polar_merge_kernel<D>, dim3((unsigned)rows), dim3(64), mp, stream);
+}
+
+polar_status merge_with_lens(const polar_problem* pr, const float* partials, int32_t num_splits,
+                             const int32_t* lens, const polar_outputs* out, void* stream) {
+  bool empty = false;
+  polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  if (num_splits < 1) return POLAR_ERR_BAD_SHAPE;
+  MergeParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  float scale_unused = 0.0f;
+  st = head_params(pr, mp.hp, mp.hp_stride, mp.floor_on, scale_unused);
+  if (st != POLAR_OK) return st;
+  if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
+  if (!partials) return POLAR_ERR_NULL_ARG;
+  if (!aligned(partials, 4)) return POLAR_ERR_MISALIGNED;
+  const void* ins[1] = {partials};
+  const size_t in_bytes[1] = {partial_bytes(pr, num_splits)};
+  st = check_outputs(pr, out, ins, in_bytes, 1);
+  if (st != POLAR_OK) return st;
+  mp.part = partials;
+  mp.lens = lens;
+  mp.dir = out->direction;
+  mp.neff = out->n_eff;
+  mp.conf = out->confidence;
+  mp.count = out->count;
+  mp.stats = out->stats;
+  mp.B = pr->batch;
+  mp.H = pr->heads;
+  mp.Tq = pr->seq_q;
+  mp.Tk = pr->seq_k;
+  mp.S = num_splits;
+  mp.causal = pr->causal != 0;
+  return pr->head_dim == 64 ? launch_merge<64>(pr, mp, stream) : launch_merge<128>(pr, mp, stream);
 }
 
 }  // namespace
@@ -254,36 +370,9 @@ size_t polar_attn_decode_workspace_bytes(const polar_problem* pr, int32_t num_sp
 
 polar_status polar_attn_merge(const polar_problem* pr, const float* partials, int32_t num_splits,
                               const polar_outputs* out, void* stream) {
-  bool empty = false;
-  polar_status st = check_shape(pr, empty);
-  if (st != POLAR_OK) return st;
-  if (num_splits < 1) return POLAR_ERR_BAD_SHAPE;
-  MergeParams mp;
-  std::memset(&mp, 0, sizeof(mp));
-  float scale_unused = 0.0f;
-  st = head_params(pr, mp.hp, mp.hp_stride, mp.floor_on, scale_unused);
-  if (st != POLAR_OK) return st;
-  if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
-  if (!partials) return POLAR_ERR_NULL_ARG;
-  if (!aligned(partials, 4)) return POLAR_ERR_MISALIGNED;
-  const void* ins[1] = {partials};
-  const size_t in_bytes[1] = {partial_bytes(pr, num_splits)};
-  st = check_outputs(pr, out, ins, in_bytes, 1);
-  if (st != POLAR_OK) return st;
-  mp.part = partials;
-  mp.dir = out->direction;
-  mp.neff = out->n_eff;
-  mp.conf = out->confidence;
-  mp.count = out->count;
-  mp.stats = out->stats;
-  mp.B = pr->batch;
-  mp.H = pr->heads;
-  mp.Tq = pr->seq_q;
-  mp.Tk = pr->seq_k;
-  mp.S = num_splits;
-  mp.causal = pr->causal != 0;
-  return pr->head_dim == 64 ? launch_merge<64>(pr, mp, stream) : launch_merge<128>(pr, mp, stream);
+  return merge_with_lens(pr, partials, num_splits, nullptr, out, stream);
 }
+
 
 polar_status polar_attn_decode(const polar_problem* pr, const void* q, const void* k_cache, const void* v_cache,
                                int32_t num_splits, void* workspace, size_t workspace_bytes,
@@ -323,7 +412,9 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
   dp.S = splits;
   dp.split_len = (pr->seq_k + splits - 1) / splits;
   const dim3 grid(splits, pr->heads, pr->batch);
-  if (pr->head_dim == 64)
+  if (pr->heads > pr->kv_heads)  // grouped: every KV row is read once per group chunk
+    st = launch_grouped_splits(pr, nullptr, q, k_cache, v_cache, splits, workspace, stream);
+  else if (pr->head_dim == 64)
     st = launch(polar::polar_decode_split_kernel<64, kDecodeWaves, kDecodeUnroll>, grid, dim3(kDecodeWaves * 64),
                 dp, stream);
   else
@@ -331,6 +422,58 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
                 dp, stream);
   if (st != POLAR_OK) return st;
   return polar_attn_merge(pr, (const float*)workspace, splits, out, stream);
+}
+
+int32_t polar_attn_decode_paged_num_splits(const polar_problem* pr, const polar_paged_kv* kv, int32_t num_splits) {
+  int splits = 0;
+  if (!pr || check_paged(pr, kv, num_splits, splits) != POLAR_OK) return 0;
+  return splits;
+}
+
+size_t polar_attn_decode_paged_workspace_bytes(const polar_problem* pr, const polar_paged_kv* kv,
+                                               int32_t num_splits) {
+  int splits = 0;
+  if (!pr || check_paged(pr, kv, num_splits, splits) != POLAR_OK) return 0;
+  return partial_bytes(pr, splits);
+}
+
+polar_status polar_attn_decode_paged(const polar_problem* pr, const void* q, const polar_paged_kv* kv,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     const polar_outputs* out, void* stream) {
+  if (!pr) return POLAR_ERR_NULL_ARG;
+  int splits = 0;
+  polar_status st = check_paged(pr, kv, num_splits, splits);
+  if (st != POLAR_OK) return st;
+  {
+    HeadParams hp;
+    int stride = 0, floor_on = 0;
+    float scale = 0.0f;
+    st = head_params(pr, hp, stride, floor_on, scale);
+    if (st != POLAR_OK) return st;
+  }
+  if (pr->batch == 0 || pr->seq_q == 0) return POLAR_OK;  // no rows: pointers may be NULL
+  if (!q || !kv->k_pool || !kv->v_pool || !kv->block_table || !kv->seq_lens) return POLAR_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(kv->k_pool, 16) || !aligned(kv->v_pool, 16) || !aligned(kv->block_table, 4) ||
+      !aligned(kv->seq_lens, 4))
+    return POLAR_ERR_MISALIGNED;
+  const size_t need = partial_bytes(pr, splits);
+  if (!workspace || workspace_bytes < need) return POLAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return POLAR_ERR_MISALIGNED;
+  const size_t qb = (size_t)pr->batch * pr->heads * pr->head_dim * 2;
+  const size_t pool_b = (size_t)kv->num_blocks * kv->block_size * pr->kv_heads * pr->head_dim * 2;
+  const size_t tab_b = (size_t)pr->batch * kv->max_blocks * 4;
+  const size_t len_b = (size_t)pr->batch * 4;
+  const void* ins[6] = {q, kv->k_pool, kv->v_pool, kv->block_table, kv->seq_lens, workspace};
+  const size_t in_bytes[6] = {qb, pool_b, pool_b, tab_b, len_b, need};
+  st = check_outputs(pr, out, ins, in_bytes, 6);
+  if (st != POLAR_OK) return st;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, need, ins[i], in_bytes[i])) return POLAR_ERR_ALIAS;
+  st = launch_grouped_splits(pr, kv, q, kv->k_pool, kv->v_pool, splits, workspace, stream);
+  if (st != POLAR_OK) return st;
+  polar_problem flat = *pr;
+  flat.causal = 0;
+  return merge_with_lens(&flat, (const float*)workspace, splits, kv->seq_lens, out, stream);
 }
 
 }  // extern "C"

@@ -68,6 +68,7 @@ struct DecodeParams {
 
 struct MergeParams {
   const float* part;  // [B, H, Tq, S, D + 3]
+  const int32_t* lens;  // optional [B]: visible count of sequence b (one query per sequence)
   float* dir;
   float* neff;
   float* conf;

@@ -78,6 +78,11 @@ WORKLOADS = {
     "bf16_decode_b64_h8_tk65536_d128": Workload(
         "bf16_decode_b64_h8_tk65536_d128", torch.bfloat16, 64, 8, 8, 1, 65536, 128, True, 1005, decode=True,
         description="Polar Attention split-KV decode, bf16, batch 64, H=8, d=128, 65536-token KV cache"),
+    "bf16_paged_decode_b64_h32_kv8_tk65536_d128": Workload(
+        "bf16_paged_decode_b64_h32_kv8_tk65536_d128", torch.bfloat16, 64, 32, 8, 1, 65536, 128, False, 1006,
+        decode=True, extra={"block_size": 16},
+        description="Polar Attention grouped split-KV decode over a paged cache, bf16, batch 64, 32 query heads "
+                    "over 8 KV heads, d=128, 65536 keys per sequence in shuffled 16-row blocks"),
 }
 
 
@@ -160,3 +165,29 @@ def decode_inputs(w: Workload, device):
         k[b] = torch.randn(w.Hkv, w.Tk, w.d, generator=g, device=dev, dtype=torch.float32).to(w.dtype)
         v[b] = torch.randn(w.Hkv, w.Tk, w.d, generator=g, device=dev, dtype=torch.float32).to(w.dtype)
     return q, k, v, {}
+
+
+def paged_decode_inputs(w: Workload, device):
+    """Paged decode workload: q [B,H,1,d]; pools [NB, block_size, Hkv, d] holding every
+    sequence's Tk keys in blocks placed at a random permutation of the pool (block table
+    [B, Tk / block_size] int32, from a CPU generator seeded with seed + 1); seq_lens [B]
+    = Tk.  The keys of sequence b are drawn like the contiguous decode workload's, from a
+    device generator seeded with seed * 1000 + b (q from seed * 1000 - 1)."""
+    dev = torch.device(device)
+    bs = w.extra["block_size"]
+    mb = w.Tk // bs
+    nb = w.B * mb
+    table = torch.randperm(nb, generator=torch.Generator().manual_seed(w.seed + 1)).view(w.B, mb)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 - 1)
+    q = torch.randn(w.B, w.H, w.Tq, w.d, generator=g, device=dev, dtype=torch.float32).to(w.dtype)
+    k_pool = torch.empty(nb, bs, w.Hkv, w.d, device=dev, dtype=w.dtype)
+    v_pool = torch.empty_like(k_pool)
+    rows = table.to(dev)
+    for b in range(w.B):
+        g.manual_seed(w.seed * 1000 + b)
+        for pool in (k_pool, v_pool):
+            x = torch.randn(w.Hkv, w.Tk, w.d, generator=g, device=dev, dtype=torch.float32).to(w.dtype)
+            pool[rows[b]] = x.view(w.Hkv, mb, bs, w.d).permute(1, 2, 0, 3)
+    lens = torch.full((w.B,), w.Tk, dtype=torch.int32, device=dev)
+    return q, k_pool, v_pool, rows.to(torch.int32), lens

@@ -69,19 +69,22 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
         "F(polar_problem, count_scale)\n"
         "F(polar_outputs, direction) F(polar_outputs, n_eff) F(polar_outputs, confidence) F(polar_outputs, count)\n"
         "F(polar_outputs, stats)\n"
+        "F(polar_paged_kv, k_pool) F(polar_paged_kv, v_pool) F(polar_paged_kv, block_table)\n"
+        "F(polar_paged_kv, seq_lens) F(polar_paged_kv, num_blocks) F(polar_paged_kv, block_size)\n"
+        "F(polar_paged_kv, max_blocks)\n"
         'printf("sizeof polar_problem %zu\\nsizeof polar_outputs %zu\\n", sizeof(polar_problem), sizeof(polar_outputs));\n'
+        'printf("sizeof polar_paged_kv %zu\\n", sizeof(polar_paged_kv));\n'
         "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    classes = {"polar_problem": pa.PolarProblem, "polar_outputs": pa.PolarOutputs, "polar_paged_kv": pa.PolarPagedKV}
     for line in filter(None, lines):
         a, b, c = line.split()
         if a == "sizeof":
-            cls = pa.PolarProblem if b == "polar_problem" else pa.PolarOutputs
-            assert ctypes.sizeof(cls) == int(c), line
+            assert ctypes.sizeof(classes[b]) == int(c), line
         else:
-            cls = pa.PolarProblem if a == "polar_problem" else pa.PolarOutputs
-            assert getattr(cls, b).offset == int(c), line
+            assert getattr(classes[a], b).offset == int(c), line
 
 
 # ---------------------------------------------------------------- argument checks (no launch)
@@ -178,10 +181,97 @@ def test_decode_and_merge_validation(lib):
     # workspace overlapping an output
     assert lib.polar_attn_decode(ctypes.byref(pr), fake(1), fake(2), fake(3), 4, fake(10), need, ctypes.byref(o),
                                  None) == 7
+    # an empty batch: split count and workspace queries and the call itself are fine
+    empty = good_problem(batch=0, seq_q=1, seq_k=1000, head_dim=128)
+    epr, ekeep = empty.to_c()
+    assert lib.polar_attn_decode_num_splits(ctypes.byref(epr), 0) == 1
+    assert lib.polar_attn_decode_workspace_bytes(ctypes.byref(epr), 0) == 0
+    assert lib.polar_attn_decode(ctypes.byref(epr), None, None, None, 0, None, 0,
+                                 ctypes.byref(pa.PolarOutputs(None, None, None, None, None)), None) == 0
     # merge
     assert lib.polar_attn_merge(ctypes.byref(pr), None, 4, ctypes.byref(o), None) == 1
     assert lib.polar_attn_merge(ctypes.byref(pr), fake(4), 0, ctypes.byref(o), None) == 2
     assert lib.polar_attn_merge(ctypes.byref(pr), fake(10), 4, ctypes.byref(o), None) == 7
+
+
+def paged(num_blocks=64, block_size=16, max_blocks=64, table=None, lens=None, kp=None, vp=None):
+    return pa.PolarPagedKV(fake(2) if kp is None else kp, fake(3) if vp is None else vp,
+                           fake(5) if table is None else table, fake(6) if lens is None else lens,
+                           num_blocks, block_size, max_blocks)
+
+
+def test_paged_decode_validation(lib):
+    prob = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128)
+    pr, keep = prob.to_c()
+    kv = paged()
+    nsplit = lib.polar_attn_decode_paged_num_splits
+    wbytes = lib.polar_attn_decode_paged_workspace_bytes
+    call = lib.polar_attn_decode_paged
+    assert nsplit(ctypes.byref(pr), ctypes.byref(kv), 0) >= 1
+    assert nsplit(ctypes.byref(pr), ctypes.byref(kv), 9) == 9
+    assert nsplit(ctypes.byref(pr), ctypes.byref(kv), 1001) == 0
+    assert nsplit(ctypes.byref(pr), None, 0) == 0
+    assert wbytes(ctypes.byref(pr), ctypes.byref(kv), 3) == 2 * 8 * 1 * 3 * 131 * 4
+    o = outputs()
+
+    def run(kvx=None, q=None, splits=4, ws=None, wsb=1 << 26, prx=None, out=None):
+        return call(ctypes.byref(pr if prx is None else prx), fake(1) if q is None else q,
+                    None if kvx is False else ctypes.byref(kv if kvx is None else kvx), splits,
+                    fake(4) if ws is None else ws, wsb, ctypes.byref(o if out is None else out), None)
+
+    assert run(kvx=False) == 1
+    assert run(q=ctypes.c_void_p(0)) == 1
+    assert call(None, fake(1), ctypes.byref(kv), 4, fake(4), 1 << 26, ctypes.byref(o), None) == 1
+    assert run(kvx=paged(table=ctypes.c_void_p(0))) == 1
+    assert run(kvx=paged(lens=ctypes.c_void_p(0))) == 1
+    assert run(kvx=paged(kp=ctypes.c_void_p(0))) == 1
+    # block size must be a power of two in 1..1024; the table must cover seq_k
+    for bs in (0, 3, 24, 2048):
+        assert run(kvx=paged(block_size=bs, max_blocks=4096)) == 2, bs
+    assert run(kvx=paged(num_blocks=0)) == 2
+    assert run(kvx=paged(max_blocks=62)) == 2          # 62 * 16 < 1000
+    assert run(kvx=paged(max_blocks=63)) != 2          # 63 * 16 >= 1000: passes this check
+    assert run(splits=1001) == 2
+    # decode problems only: one query per sequence, bf16
+    two = good_problem(batch=2, heads=8, kv_heads=2, seq_q=2, seq_k=1000, causal=False, head_dim=128)
+    tpr, tkeep = two.to_c()
+    assert run(prx=tpr) == 3
+    f32 = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128,
+                       dtype=pa.POLAR_F32)
+    fpr, fkeep = f32.to_c()
+    assert run(prx=fpr) == 3
+    # alignment
+    assert run(kvx=paged(table=ctypes.c_void_p(FAKE + 5 * (1 << 34) + 2))) == 5
+    assert run(kvx=paged(kp=ctypes.c_void_p(FAKE + 2 * (1 << 34) + 8))) == 5
+    assert run(ws=ctypes.c_void_p(FAKE + 4 * (1 << 34) + 4)) == 5
+    # workspace missing or short
+    need = wbytes(ctypes.byref(pr), ctypes.byref(kv), 4)
+    assert run(ws=ctypes.c_void_p(0)) == 6
+    assert run(wsb=need - 1) == 6
+    # aliasing: workspace over the block table; an output over the lengths
+    assert run(ws=fake(5)) == 7
+    assert run(out=outputs(n_eff=fake(6))) == 7
+    # an empty batch is accepted without pointers
+    empty = good_problem(batch=0, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128)
+    epr, ekeep = empty.to_c()
+    assert call(ctypes.byref(epr), None, ctypes.byref(paged(table=ctypes.c_void_p(0), lens=ctypes.c_void_p(0),
+                                                             kp=ctypes.c_void_p(0), vp=ctypes.c_void_p(0))),
+                0, None, 0, ctypes.byref(pa.PolarOutputs(None, None, None, None, None)), None) == 0
+
+
+def test_grouped_auto_splits_count_group_chunks(lib):
+    """A grouped workgroup serves up to 8 query heads of a group, so the automatic split
+    count is sized by (batch x kv_heads x chunks) workgroups."""
+    mha = good_problem(batch=2, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    gqa = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    g3 = good_problem(batch=2, heads=6, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    n = {}
+    for name, prob in (("mha", mha), ("gqa", gqa), ("g3", g3)):
+        pr, keep = prob.to_c()
+        n[name] = lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0)
+    assert n["mha"] == 4096 // 16          # 16 (b, h) rows
+    assert n["gqa"] == 4096 // 2 // 2 // 1  # 2 x 2 kv heads x 1 chunk of 4
+    assert n["g3"] == -(-4096 // (2 * 6))   # group of 3 runs one head per workgroup
 
 
 def test_python_binding_checks():
