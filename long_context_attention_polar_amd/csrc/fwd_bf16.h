@@ -24,11 +24,13 @@
 //     0-3, 8-11, 4-7, 12-15; the matching V^T operand comes straight from the row-major
 //     V tile through two ds_read_b64_tr_b16 transpose reads, each delivering four
 //     consecutive keys of one dimension to a lane.
-//   * A tile is two 32-key blocks.  The reference maximum moves only when a score
-//     exceeds it by more than 2^8 (base 2), decided for the whole wave with one ballot
-//     per block; only then are the two halves of a row exchanged and sum p, sum p^2 (by
-//     alpha^2) and acc rescaled.  The true maximum is tracked on the side for the
-//     reported statistics.
+//   * The weights of a tile are formed against the current reference maximum, with no
+//     maximum taken first.  When some lane's weights of the tile sum to more than 2^8 (so
+//     a weight may exceed 2^8; always on the wave's first tile), the wave moves the
+//     reference of its rows to the tile maximum, rescales sum p and acc by alpha and
+//     sum p^2 by alpha^2, and forms the tile's weights again from its scores, which are
+//     still in registers.  Later moves happen only when a row's maximum grows by more
+//     than 2^8.  The variant that reports statistics tracks the true maximum on the side.
 //   * sum p and sum p^2 are taken from the same bf16-rounded weights that enter P V, two
 //     at a time with v_dot2_f32_bf16 (exact products, fp32 sums), as per-lane partial
 //     sums combined once in the epilogue.
@@ -99,7 +101,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int kv0, 
   }
 }
 
-template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL>
+template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL, bool STATS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_fwd_bf16_kernel(
     const FwdParams p) {
   static_assert(BN == 32 || BN == 64, "key tile");
@@ -237,10 +239,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], s[nb][mb], 0, 0, 0);
       }
     bf16x8 pf[NB][PS];
+    // ---- mask on the diagonal / tail tiles only (in place)
+    if (kv0 + BN - 1 > wave_kmin) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      // ---- mask on the diagonal / tail tiles only (in place)
-      if (kv0 + BN - 1 > wave_kmin) {
+      for (int nb = 0; nb < NB; ++nb) {
         const int lim = kmax[nb] - kv0 - 4 * half;  // key offset limit for this lane
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -250,14 +252,60 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             for (int j = 0; j < 4; ++j)
               if (mb * 32 + 8 * i + j > lim) s[nb][mb][4 * i + j] = -INFINITY;
       }
-      // ---- a4: tile maximum; move the reference only when a score exceeds it by 2^8
-      float mx = s[nb][0][0];
+    }
+    // ---- a5: p = exp2(c s - m_ref) rounded to bf16 in the B-operand order; the tile's sum p
+    // and sum p^2 are taken from the same bf16 weights, two at a time (exact products,
+    // fp32 sums)
+    float t1[NB], t2[NB];
+    auto weights = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float neg_m = -m_ref[nb];
+        float a1[2] = {0.0f, 0.0f}, a2[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+              bf16x2 pp;
+              pp[0] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j], neg_m));
+              pp[1] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j + 1], neg_m));
+              a1[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, a1[j >> 1], false);
+              a2[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, a2[j >> 1], false);
+              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
+              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = pp[1];
+            }
+        t1[nb] = a1[0] + a1[1];
+        t2[nb] = a2[0] + a2[1];
+      }
+    };
+    auto lane_max = [&](int nb) __attribute__((always_inline)) {
+      float a = s[nb][0][0], b2 = s[nb][0][1];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = (mb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][mb][e]);
-      t_max[nb] = fmaxf(t_max[nb], mx);
-      if (__ballot(c[nb] * mx > m_ref[nb] + kRescaleSlack) != 0) {
+        for (int e = (mb == 0 ? 2 : 0); e < 16; e += 2) {
+          a = fmaxf(a, s[nb][mb][e]);
+          b2 = fmaxf(b2, s[nb][mb][e + 1]);
+        }
+      return fmaxf(a, b2);
+    };
+    weights();
+    if constexpr (STATS) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) t_max[nb] = fmaxf(t_max[nb], lane_max(nb));
+    }
+    // ---- a4: some weight of the wave may exceed 2^8 (a lane's tile sum does; always on
+    // the wave's first tile): move the reference of the rows to the tile maximum,
+    // rescale sum p and acc by alpha and sum p^2 by alpha^2, and form the weights again
+    bool big = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) big |= t1[nb] > kWeightLimit;
+    if (__ballot(big) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float mx = lane_max(nb);
         const float row_max = fmaxf(mx, xor32(mx));
         const float m_new = fmaxf(m_ref[nb], c[nb] * row_max);
         const float alpha = fast_exp2(m_ref[nb] - m_new);
@@ -273,24 +321,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           for (int e = 0; e < 16; ++e) o[nb][dm][e] *= alpha;
         m_ref[nb] = m_new;
       }
-      // ---- a5: p = exp2(c s - m) rounded to bf16 in the B-operand order; sum p and
-      // sum p^2 are taken from the same bf16 weights, two at a time (exact products,
-      // fp32 sums)
-      const float neg_m = -m_ref[nb];
+      weights();
+    }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; j += 2) {
-            bf16x2 pp;
-            pp[0] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j], neg_m));
-            pp[1] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j + 1], neg_m));
-            s1[nb][j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, s1[nb][j >> 1], false);
-            s2[nb][j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, s2[nb][j >> 1], false);
-            pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
-            pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = pp[1];
-          }
+    for (int nb = 0; nb < NB; ++nb) {
+      s1[nb][0] += t1[nb];
+      s2[nb][0] += t2[nb];
     }
     // ---- a6: O^T += V^T P^T; each V fragment feeds the NB query blocks
 #pragma unroll
@@ -327,17 +363,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     __syncthreads();
   }
 
-  // ---- a7: combine the two halves of each row, form the channels [ATMA §2.1]
+  // ---- a7: combine the two halves of each row and form the channels [ATMA §2.1].
+  // n_eff, the confidence and the direction do not depend on the reference, so they are
+  // formed from the sums relative to it; the statistics, when requested, are brought to
+  // the true maximum, which that variant tracks on the side.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float S1 = s1[nb][0] + s1[nb][1];
     float S2 = s2[nb][0] + s2[nb][1];
     S1 += xor32(S1);
     S2 += xor32(S2);
-    const float m_true = c[nb] * fmaxf(t_max[nb], xor32(t_max[nb]));
-    const float to_true = fast_exp2(m_ref[nb] - m_true);
-    S1 *= to_true;
-    S2 *= to_true * to_true;
+    const float row_tmax = STATS ? fmaxf(t_max[nb], xor32(t_max[nb])) : 0.0f;  // all lanes take part
     float nn = 0.0f;
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
@@ -357,17 +393,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           *(f32x4*)(drow + dm * 32 + 8 * i + 4 * half) = val;
         }
       if (half == 0) {
-        const float m_nat = m_true * kLn2;
         float neff, conf, count;
-        magnitude_channel(m_nat, S1, S2, n_vis[nb], lam[nb], p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff,
-                          conf, count);
+        magnitude_channel(m_ref[nb] * kLn2, S1, S2, n_vis[nb], lam[nb], p.floor_on != 0, p.hp.beta[hpi],
+                          p.hp.kinv[hpi], neff, conf, count);
         p.neff[row] = neff;
         if (p.conf) p.conf[row] = conf;
         if (p.count) p.count[row] = count;
-        if (p.stats) {
-          p.stats[row * 3 + 0] = m_nat;
-          p.stats[row * 3 + 1] = S1;
-          p.stats[row * 3 + 2] = S2;
+        if constexpr (STATS) {
+          const float m_true = c[nb] * row_tmax;
+          const float to_true = fast_exp2(m_ref[nb] - m_true);
+          p.stats[row * 3 + 0] = m_true * kLn2;
+          p.stats[row * 3 + 1] = S1 * to_true;
+          p.stats[row * 3 + 2] = S2 * to_true * to_true;
         }
       }
     }

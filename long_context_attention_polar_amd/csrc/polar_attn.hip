@@ -142,7 +142,11 @@ polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
     if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
     constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
     constexpr int BN = D == 64 ? kBf16Bn_d64 : kBf16Bn_d128;
-    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL>, dim3((unsigned)blocks),
+    // the variant without statistics does not track the true row maximum
+    if (fp.stats)
+      return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, true>, dim3((unsigned)blocks),
+                    dim3(kBf16Waves * 64), fp, stream);
+    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, false>, dim3((unsigned)blocks),
                   dim3(kBf16Waves * 64), fp, stream);
   }
   fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;

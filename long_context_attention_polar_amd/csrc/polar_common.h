@@ -28,6 +28,9 @@ constexpr float kMaxInit = -1.0e30f;
 // than this (base 2), so weights stay below 2^8 between moves.  The statistics are
 // exact for any reference; the true maximum is tracked on the side.
 constexpr float kRescaleSlack = 8.0f;
+// The same bound as a weight: the bf16 prefill kernel moves its reference when a lane's
+// weights of one tile sum to more than 2^8 (every weight is then at most 2^8).
+constexpr float kWeightLimit = 256.0f;
 
 // Per-head parameters, copied by value into the kernel arguments.
 struct HeadParams {
