@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 2
+#define POLAR_ABI_VERSION 3
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -112,6 +112,24 @@ typedef struct polar_outputs {
  * non-causal, seq_q <= seq_k when causal (rows aligned to the end of the keys). */
 polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const void* k,
                             const void* v, const polar_outputs* out, void* stream);
+
+/* Partial forward for chunked prefill [ATMA §2.2: the streaming statistics of disjoint
+ * key ranges merge with weights w and w^2].  Same inputs and masking as polar_attn_fwd
+ * (causal: key j of this call visible to row i iff j <= i + seq_k - seq_q), but instead
+ * of the channels it writes, for every query row, the statistics (m, S1, S2, acc) of the
+ * keys of this call into slot `split` of DEVICE `partials` [B, heads, seq_q, num_splits,
+ * head_dim + 3] fp32 (the layout polar_attn_merge reads; m in natural-log units, S1, S2
+ * and acc relative to exp(m)).  context_k > 0 says this call is one piece of a causal
+ * context of context_k keys ending at the last query row: the length temperature of row
+ * i then uses that context's visible count i + 1 + context_k - seq_q, so pieces computed
+ * separately (a cached prefix without mask, the new chunk with the causal mask) merge
+ * into exactly what one pass over the whole context computes; merge them with a
+ * problem of seq_k = context_k, causal.  context_k = 0 uses the row's own visible count.
+ * Requires context_k >= seq_q when nonzero and 1 + tau_h ln(context_k) > 0.  Slots other
+ * than `split` are not touched; a slot that never receives a piece must hold m = -inf. */
+polar_status polar_attn_fwd_partial(const polar_problem* problem, const void* q, const void* k, const void* v,
+                                    int32_t context_k, float* partials, int32_t num_splits, int32_t split,
+                                    void* stream);
 
 /* Split count the decode will use for `num_splits` (0 = automatic choice); 0 when the
  * problem is invalid for decode. */

@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_decode_num_splits.restype = ctypes.c_int32
     lib.polar_attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.polar_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.polar_attn_fwd_partial.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.polar_attn_fwd_partial.restype = ctypes.c_int
     K = ctypes.POINTER(PolarPagedKV)
     lib.polar_attn_decode_paged.argtypes = [P, vp, K, ctypes.c_int32, vp, ctypes.c_size_t, O, vp]
     lib.polar_attn_decode_paged.restype = ctypes.c_int
@@ -220,6 +222,32 @@ def fwd(q, k, v, *, causal=True, len_temp=None, null_bias=None, count_scale=None
     return out
 
 
+def fwd_partial(q, k, v, *, causal=True, context_k=0, partials=None, num_splits=1, split=0, len_temp=None,
+                null_bias=None, count_scale=None, softmax_scale=None):
+    """Partial forward (polar_attn_fwd_partial): writes the (m, S1, S2, acc) rows of this
+    call's keys into slot `split` of partials [B,H,Tq,num_splits,d+3] fp32 (allocated, with
+    m = -inf everywhere, when not given) and returns it.  context_k: keys of the whole
+    causal context this call is a piece of (0: the call is the whole context)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, dev)
+    if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match each other and q's dtype")
+    prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
+                       softmax_scale=softmax_scale)
+    shape = (prob.batch, prob.heads, prob.seq_q, num_splits, prob.head_dim + 3)
+    if partials is None:
+        partials = torch.zeros(shape, dtype=torch.float32, device=dev)
+        partials[..., 0] = float("-inf")
+    elif tuple(partials.shape) != shape or partials.dtype != torch.float32:
+        raise ValueError(f"partials must be float32 {shape}")
+    _check_tensor("partials", partials, dev)
+    pr, keep = prob.to_c()
+    _check(load_library().polar_attn_fwd_partial(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), int(context_k),
+                                                 _ptr(partials), num_splits, split, _stream(dev)))
+    return partials
+
+
 def decode_num_splits(prob: Problem, num_splits: int = 0) -> int:
     pr, keep = prob.to_c()
     return int(load_library().polar_attn_decode_num_splits(ctypes.byref(pr), num_splits))
@@ -345,6 +373,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["fwd", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["fwd", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     qrow[nb] = wq0 + nb * 32 + col;
-    n_vis[nb] = visible_keys(qrow[nb], Tq, Tk, CAUSAL);
+    n_vis[nb] = context_count(qrow[nb], Tq, Tk, CAUSAL, p.ctx_k);
     lam[nb] = length_temperature(p.hp.tau[hpi], n_vis[nb]);
     c[nb] = lam[nb] * p.scale * kLog2e;
     kmax[nb] = CAUSAL ? min(qrow[nb] + off, Tk - 1) : Tk - 1;
@@ -381,6 +381,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
       for (int e = 0; e < 16; ++e) nn = fmaf(o[nb][dm][e], o[nb][dm][e], nn);
     nn += xor32(nn);
     const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+    if (STATS && p.part) {
+      // partial mode: the statistics of this call's keys relative to their true maximum
+      if (qrow[nb] < Tq) {
+        const float m_true = c[nb] * row_tmax;
+        const float to_true = fast_exp2(m_ref[nb] - m_true);
+        const size_t row = (size_t)bh * Tq + qrow[nb];
+        float* out = p.part + (row * p.part_S + p.part_s) * (D + 3);
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[3 + dm * 32 + 8 * i + 4 * half + j] = o[nb][dm][4 * i + j] * to_true;
+        if (half == 0) {
+          out[0] = m_true * kLn2;
+          out[1] = S1 * to_true;
+          out[2] = S2 * to_true * to_true;
+        }
+      }
+      continue;
+    }
     if (qrow[nb] < Tq) {
       const size_t row = (size_t)bh * Tq + qrow[nb];
       float* drow = p.dir + row * D;
@@ -399,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         p.neff[row] = neff;
         if (p.conf) p.conf[row] = conf;
         if (p.count) p.count[row] = count;
-        if constexpr (STATS) {
+        if (STATS && p.stats) {
           const float m_true = c[nb] * row_tmax;
           const float to_true = fast_exp2(m_ref[nb] - m_true);
           p.stats[row * 3 + 0] = m_true * kLn2;

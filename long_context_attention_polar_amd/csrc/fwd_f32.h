@@ -35,7 +35,7 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
   const float* vb = (const float*)p.v + (size_t)(b * p.Hkv + hk) * Tk * D;
 
   const int hpi = h * p.hp_stride;
-  const int n_vis = visible_keys(qrow, Tq, Tk, CAUSAL);
+  const int n_vis = context_count(qrow, Tq, Tk, CAUSAL, p.ctx_k);
   const float lam = length_temperature(p.hp.tau[hpi], n_vis);
   const float c = lam * p.scale * kLog2e;
   const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
@@ -96,7 +96,16 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
     }
   }
 
-  if (qrow < Tq) {
+  if (qrow < Tq && p.part) {
+    // partial mode: the statistics of this call's keys relative to their true maximum
+    const float to_true = fast_exp2(m_ref - m_true);
+    float* out = p.part + (((size_t)bh * Tq + qrow) * p.part_S + p.part_s) * (D + 3);
+    out[0] = m_true * kLn2;
+    out[1] = s1 * to_true;
+    out[2] = s2 * to_true * to_true;
+#pragma unroll
+    for (int e = 0; e < D; ++e) out[3 + e] = acc[e] * to_true;
+  } else if (qrow < Tq) {
     const float to_true = fast_exp2(m_ref - m_true);
     const float S1 = s1 * to_true;
     const float S2 = s2 * to_true * to_true;

@@ -143,7 +143,7 @@ polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
     constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
     constexpr int BN = D == 64 ? kBf16Bn_d64 : kBf16Bn_d128;
     // the variant without statistics does not track the true row maximum
-    if (fp.stats)
+    if (fp.stats || fp.part)
       return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, true>, dim3((unsigned)blocks),
                     dim3(kBf16Waves * 64), fp, stream);
     return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, false>, dim3((unsigned)blocks),
@@ -478,6 +478,51 @@ polar_status polar_attn_decode_paged(const polar_problem* pr, const void* q, con
   polar_problem flat = *pr;
   flat.causal = 0;
   return merge_with_lens(&flat, (const float*)workspace, splits, kv->seq_lens, out, stream);
+}
+
+polar_status polar_attn_fwd_partial(const polar_problem* pr, const void* q, const void* k, const void* v,
+                                    int32_t context_k, float* partials, int32_t num_splits, int32_t split,
+                                    void* stream) {
+  bool empty = false;
+  polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  FwdParams fp;
+  std::memset(&fp, 0, sizeof(fp));
+  st = head_params(pr, fp.hp, fp.hp_stride, fp.floor_on, fp.scale);
+  if (st != POLAR_OK) return st;
+  if (num_splits < 1 || split < 0 || split >= num_splits) return POLAR_ERR_BAD_SHAPE;
+  if (context_k != 0) {
+    if (context_k < pr->seq_q || context_k < 0) return POLAR_ERR_BAD_SHAPE;
+    // the temperature must stay positive at the longest context count
+    const int nh = pr->len_temp ? pr->heads : 0;
+    for (int h = 0; h < nh; ++h)
+      if (!(1.0 + (double)pr->len_temp[h] * std::log((double)context_k) > 0.0)) return POLAR_ERR_BAD_PARAM;
+  }
+  if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
+  if (!q || !k || !v || !partials) return POLAR_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return POLAR_ERR_MISALIGNED;
+  if (!aligned(partials, 4)) return POLAR_ERR_MISALIGNED;
+  const size_t eb = elem_bytes(pr->dtype);
+  const size_t qb = (size_t)pr->batch * pr->heads * pr->seq_q * pr->head_dim * eb;
+  const size_t kvb = (size_t)pr->batch * pr->kv_heads * pr->seq_k * pr->head_dim * eb;
+  const size_t pb = partial_bytes(pr, num_splits);
+  if (overlaps(partials, pb, q, qb) || overlaps(partials, pb, k, kvb) || overlaps(partials, pb, v, kvb))
+    return POLAR_ERR_ALIAS;
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.part = partials;
+  fp.part_S = num_splits;
+  fp.part_s = split;
+  fp.ctx_k = context_k;
+  fp.B = pr->batch;
+  fp.H = pr->heads;
+  fp.Hkv = pr->kv_heads;
+  fp.Tq = pr->seq_q;
+  fp.Tk = pr->seq_k;
+  if (pr->head_dim == 64)
+    return pr->causal ? launch_fwd<64, true>(pr, fp, stream) : launch_fwd<64, false>(pr, fp, stream);
+  return pr->causal ? launch_fwd<128, true>(pr, fp, stream) : launch_fwd<128, false>(pr, fp, stream);
 }
 
 }  // extern "C"

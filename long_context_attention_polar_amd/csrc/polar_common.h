@@ -53,8 +53,12 @@ struct FwdParams {
   int floor_on;   // null floor on
   int hp_stride;  // 1: per-head tables, 0: entry 0 serves every head
   float scale;    // softmax scale
+  float* part;    // partial mode: rows [B, H, Tq, part_S, D + 3] = (m, S1, S2, acc); no channels
+  int part_S, part_s;
+  int ctx_k;      // > 0: a row's visible count is that of a causal row over ctx_k keys
   HeadParams hp;
 };
+
 
 struct DecodeParams {
   const void* q;
@@ -90,6 +94,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int visible_keys(int row, int Tq, int Tk, bool causal) {
   int n = causal ? min(row + 1 + (Tk - Tq), Tk) : Tk;
   return max(n, 1);
+}
+
+// Visible count of query row `row` for the length temperature and the floor: its own
+// count, or, in a piece of a longer causal context of ctx_k keys (chunked prefill), the
+// count of that row in the whole context.
+__device__ __forceinline__ int context_count(int row, int Tq, int Tk, bool causal, int ctx_k) {
+  if (ctx_k > 0) return max(min(row + 1 + (ctx_k - Tq), ctx_k), 1);
+  return visible_keys(row, Tq, Tk, causal);
 }
 
 // Length temperature lam(n) = 1 + tau ln n [ATMA §2.1, direction channel].

@@ -274,6 +274,22 @@ def test_grouped_auto_splits_count_group_chunks(lib):
     assert n["g3"] == -(-4096 // (2 * 6))   # group of 3 runs one head per workgroup
 
 
+def test_fwd_partial_validation(lib):
+    prob = good_problem(seq_q=64, seq_k=64, head_dim=128, len_temp=[0.1, -0.1])
+    pr, keep = prob.to_c()
+    call = lib.polar_attn_fwd_partial
+    assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, None, 2, 0, None) == 1
+    assert call(ctypes.byref(pr), None, fake(2), fake(3), 1000, fake(4), 2, 0, None) == 1
+    for ns, sp in ((0, 0), (2, 2), (2, -1)):
+        assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, fake(4), ns, sp, None) == 2
+    assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 63, fake(4), 2, 0, None) == 2      # < seq_q
+    # tau = -0.1 is fine at 64 keys but lambda(1e6) = 1 - 0.1 ln 1e6 < 0
+    assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000000, fake(4), 2, 0, None) == 4
+    assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, ctypes.c_void_p(FAKE + 4 * (1 << 34) + 2), 2, 0,
+                None) == 5
+    assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, fake(2), 2, 0, None) == 7  # over k
+
+
 def test_python_binding_checks():
     with pytest.raises(ValueError):
         good_problem(len_temp=[0.0]).to_c()
