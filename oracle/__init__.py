@@ -5,3 +5,6 @@ package; the GPU library does not, and the two share no code.
 """
 from .polar_oracle import *  # noqa: F401,F403
 from .polar_oracle import __all__  # noqa: F401
+from .polar_backward import polar_attention_backward, row_coefficients  # noqa: F401,E402
+
+__all__ = list(__all__) + ["polar_attention_backward", "row_coefficients"]
