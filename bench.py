@@ -10,7 +10,10 @@ already resident in HBM:
     65536-token KV cache;
   * grouped split-KV decode + merge over a paged cache, bf16, batch 64, 32 query heads
     over 8 KV heads, d=128, 65536 keys per sequence in shuffled 16-row blocks (reported
-    beside the headline, not part of it).
+    beside the headline, not part of it);
+  * backward (dq, dk, dv for upstream gradients of all four channels), bf16 inputs,
+    B=1, 16 query heads over 4 KV heads, T=16384, d=128, causal (reported beside the
+    headline, not part of it, and timed in a loop of its own after the steps).
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -35,6 +38,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
 DECODE = "bf16_decode_b64_h8_tk65536_d128"
 PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
+BWD = "bf16_bwd_b1_h16_kv4_t16384_d128"
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 2.4 GHz x 256 flop/clk
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -49,6 +54,12 @@ def source_digest():
 
 def prefill_flops(w):
     return 4 * w.d * w.pairs()
+
+
+def backward_flops(w):
+    """Algorithmic flops of the backward: 10 d per computed (query, key) pair -- the
+    scores, <w, v_j>, and the three products into dq, dk and dv (2 d each)."""
+    return 10 * w.d * w.pairs()
 
 
 def decode_bytes(w):
@@ -167,27 +178,53 @@ def main():
     kwp = dict(seq_k=wp.Tk, len_temp=wp.len_temp(), null_bias=wp.null_bias(), count_scale=wp.count_scale())
     parts.append(dict(name=PAGED, w=wp, kind="decode", bytes=decode_bytes(wp), headline=False,
                       run=lambda: pa.decode_paged(qp, kpool, vpool, table, lens, workspace=wsp, out=outp, **kwp)))
+    wb = pin.WORKLOADS[BWD]
+    qb, kb, vb, _ = pin.workload_inputs(wb, dev)
+    grb = {n: t.to(dev) for n, t in pin.random_grads(wb.B, wb.H, wb.Tq, wb.d, wb.extra["grad_seed"]).items()}
+    probb = pa.problem_for(qb, kb, causal=True, len_temp=wb.len_temp(), null_bias=wb.null_bias(),
+                           count_scale=wb.count_scale())
+    wsb = torch.empty(pa.bwd_workspace_bytes(probb), dtype=torch.uint8, device=dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    outb = {"dq": torch.empty(qb.shape, **f32), "dk": torch.empty(kb.shape, **f32), "dv": torch.empty(vb.shape, **f32)}
+    kwb = dict(causal=True, len_temp=wb.len_temp(), null_bias=wb.null_bias(), count_scale=wb.count_scale())
+    parts.append(dict(name=BWD, w=wb, kind="backward", flops=backward_flops(wb), headline=False, separate=True,
+                      run=lambda: pa.bwd(qb, kb, vb, grb, workspace=wsb, out=outb, **kwb)))
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         for p in parts:
-            p["run"]()
+            if not p.get("separate"):
+                p["run"]()
     torch.cuda.synchronize()
 
     events = {p["name"]: [] for p in parts}
+
+    def timed(p):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        p["run"]()
+        e1.record()
+        events[p["name"]].append((e0, e1))
+
+    step_parts = [p for p in parts if not p.get("separate")]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for p in parts:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            p["run"]()
-            e1.record()
-            events[p["name"]].append((e0, e1))
+        for p in step_parts:
+            timed(p)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # parts outside the step (the backward) are timed afterwards in their own loop, so
+    # their long vector-ALU load does not change the clocks the step parts run at
+    for p in parts:
+        if p.get("separate"):
+            for _ in range(args.warmup):
+                p["run"]()
+            for _ in range(args.steps):
+                timed(p)
+    torch.cuda.synchronize()
 
     res = {}
     for p in parts:
@@ -199,6 +236,10 @@ def main():
             entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
             entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
             entry["flops_per_launch"] = p["flops"]
+        elif p["kind"] == "backward":
+            entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
+            entry["frac_f32_valu_peak"] = entry["tflops"] / PEAK_F32_VALU_TFLOPS
+            entry["flops_per_call"] = p["flops"]
         else:
             entry["gbs"] = p["bytes"] / (avg * 1e-3) / 1e9
             entry["frac_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS
@@ -232,6 +273,9 @@ def main():
         "paged_gqa_decode": {"bound": "hbm", "achieved": res[PAGED]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": res[PAGED]["frac_hbm_peak"], "ms": res[PAGED]["ms_avg"],
                              "note": "32 query heads share 8 KV heads; K and V are read once per group"},
+        "backward": {"bound": "alu", "achieved": res[BWD]["tflops"], "peak": PEAK_F32_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": res[BWD]["frac_f32_valu_peak"], "ms": res[BWD]["ms_avg"],
+                     "note": "three fp32 vector-ALU kernels; 10 d algorithmic flops per causal pair"},
         "parts": res,
         "source_digest": digest,
     }

@@ -46,7 +46,8 @@
  *              launch failure seen right after the launch; faults inside a kernel
  *              surface at the caller's next synchronisation.
  *   Empty      batch == 0 or seq_q == 0 is valid and enqueues nothing; the data
- *              pointers of such a call may be NULL.
+ *              pointers of such a call may be NULL (polar_attn_bwd with seq_q == 0
+ *              still writes zero dk and dv).
  */
 #ifndef POLAR_ATTN_H
 #define POLAR_ATTN_H
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 3
+#define POLAR_ABI_VERSION 4
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -200,6 +201,50 @@ polar_status polar_attn_decode_paged(const polar_problem* problem, const void* q
  * causal, i + 1 + seq_k - seq_q when causal).  dtype is ignored. */
 polar_status polar_attn_merge(const polar_problem* problem, const float* partials,
                               int32_t num_splits, const polar_outputs* out, void* stream);
+
+/* Upstream gradients of the four forward channels for polar_attn_bwd.  Each is a DEVICE
+ * fp32 array laid out like the matching forward output (d_direction [B, heads, seq_q,
+ * head_dim], 16-byte aligned; the others [B, heads, seq_q], 4-byte aligned); NULL means
+ * zero. */
+typedef struct polar_grads {
+  const float* d_direction;
+  const float* d_n_eff;
+  const float* d_confidence;
+  const float* d_count;
+} polar_grads;
+
+/* Bytes of device workspace polar_attn_bwd needs: B * heads * seq_q * (head_dim + 4)
+ * fp32 (per query row, the vector w and four row constants).  0 when the problem is
+ * invalid (or has no query rows). */
+size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
+
+/* Backward of polar_attn_fwd: the gradients of
+ *   L = sum d_direction . direction + sum d_n_eff n_eff + sum d_confidence confidence
+ *       + sum d_count count
+ * with respect to q, k and v, by the chain rule through the definition above (the ATMA
+ * summary trains with the operator [ATMA §3] but gives no backward; the length
+ * temperature and the null floor depend on the visible count only, so they carry no
+ * gradient).  Per row i, with weights p_ij = exp(s_ij - m_i), S1, S2, acc and u as in
+ * the forward:
+ *   T = tanh(ln n_eff / kappa),  G_conf = d_confidence + d_count T,
+ *   G_neff = d_n_eff + d_count confidence (1 - T^2) / (kappa n_eff),
+ *   c1 = (2 G_neff n_eff + G_conf confidence (1 - confidence)) / S1  (the second term is
+ *        0 when the floor is off),   c2 = -G_neff n_eff / S2,
+ *   w  = (d_direction - u (u . d_direction)) / ||acc||  (0 when acc == 0),
+ *   ds_ij = p_ij (c1 + 2 c2 p_ij + <w, v_j>),
+ *   dq_i = lam_i scale sum_j ds_ij k_j,  dk_j = sum_i lam_i scale ds_ij q_i,  dv_j = sum_i p_ij w_i,
+ * dk and dv summed over the query heads that share a KV head.  Same problem rules as
+ * polar_attn_fwd (bf16 or fp32 inputs, head_dim 64 or 128, causal or not); fp32
+ * arithmetic; batch * heads <= 65535.  Outputs are DEVICE fp32, 16-byte aligned and
+ * overwritten: dq [B, heads, seq_q, head_dim], dk and dv [B, kv_heads, seq_k, head_dim].
+ * `workspace` (DEVICE, 16-byte aligned, polar_attn_bwd_workspace_bytes bytes) is
+ * scratch owned by the call until the stream reaches its end.  No output or the
+ * workspace may overlap an input or another output.  batch == 0 enqueues nothing;
+ * seq_q == 0 (q, dq and workspace may then be NULL) writes zero dk and dv.  Three
+ * kernels run in order on `stream`. */
+polar_status polar_attn_bwd(const polar_problem* problem, const void* q, const void* k, const void* v,
+                            const polar_grads* grads, float* dq, float* dk, float* dv, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* polar_status_string(polar_status status);

@@ -5,6 +5,7 @@ arguments.  PyTorch provides device memory and the current stream.  The entry po
 mirror the C ABI in include/polar_attn.h:
 
     fwd(q, k, v, ...)            -> polar_attn_fwd      (fused prefill forward)
+    bwd(q, k, v, grads, ...)     -> polar_attn_bwd      (dq, dk, dv of the forward)
     decode(q, k_cache, v_cache)  -> polar_attn_decode   (split-KV decode + merge)
     merge(partials, ...)         -> polar_attn_merge    (merge of split statistics)
     decode_num_splits / decode_workspace_bytes / status_string / abi_version
@@ -47,6 +48,11 @@ class PolarPagedKV(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("seq_lens", ctypes.c_void_p), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32)]
+
+
+class PolarGrads(ctypes.Structure):
+    _fields_ = [("d_direction", ctypes.c_void_p), ("d_n_eff", ctypes.c_void_p), ("d_confidence", ctypes.c_void_p),
+                ("d_count", ctypes.c_void_p)]
 
 
 class PolarError(RuntimeError):
@@ -92,6 +98,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_decode_paged_num_splits.restype = ctypes.c_int32
     lib.polar_attn_decode_paged_workspace_bytes.argtypes = [P, K, ctypes.c_int32]
     lib.polar_attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+    Gr = ctypes.POINTER(PolarGrads)
+    lib.polar_attn_bwd.argtypes = [P, vp, vp, vp, Gr, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.polar_attn_bwd.restype = ctypes.c_int
+    lib.polar_attn_bwd_workspace_bytes.argtypes = [P]
+    lib.polar_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.polar_status_string.argtypes = [ctypes.c_int]
     lib.polar_status_string.restype = ctypes.c_char_p
     lib.polar_abi_version.argtypes = []
@@ -352,6 +363,60 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, seq_k=None, num_sp
     return out
 
 
+GRAD_NAMES = ("direction", "n_eff", "confidence", "count")
+
+
+def bwd_workspace_bytes(prob: Problem) -> int:
+    pr, keep = prob.to_c()
+    return int(load_library().polar_attn_bwd_workspace_bytes(ctypes.byref(pr)))
+
+
+def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
+        workspace=None, out=None):
+    """Backward of the forward (polar_attn_bwd): gradients of
+    sum(grads["direction"] * direction) + sum(grads["n_eff"] * n_eff) + ... with respect to
+    q, k, v.  grads maps any of "direction" [B,H,Tq,d], "n_eff", "confidence", "count"
+    [B,H,Tq] to fp32 tensors on q's device (a missing entry is zero).  Returns a dict with
+    dq [B,H,Tq,d] and dk, dv [B,Hkv,Tk,d], fp32.  Work is enqueued on the current stream."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, dev)
+    if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match each other and q's dtype")
+    unknown = set(grads) - set(GRAD_NAMES)
+    if unknown:
+        raise ValueError(f"unknown gradient names {sorted(unknown)}")
+    prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
+                       softmax_scale=softmax_scale)
+    row_shape = (prob.batch, prob.heads, prob.seq_q)
+    for name in GRAD_NAMES:
+        t = grads.get(name)
+        if t is None:
+            continue
+        shape = tuple(q.shape) if name == "direction" else row_shape
+        if tuple(t.shape) != shape or t.dtype != torch.float32:
+            raise ValueError(f"grads[{name!r}] must be float32 {shape}")
+        _check_tensor(f"grads[{name!r}]", t, dev)
+    g = PolarGrads(*[_ptr(grads.get(name)) for name in GRAD_NAMES])
+    need = bwd_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, dev)
+    if out is None:
+        f = dict(device=dev, dtype=torch.float32)
+        out = {"dq": torch.empty(q.shape, **f), "dk": torch.empty(k.shape, **f), "dv": torch.empty(v.shape, **f)}
+    for name, like in (("dq", q), ("dk", k), ("dv", v)):
+        t = out[name]
+        if tuple(t.shape) != tuple(like.shape) or t.dtype != torch.float32:
+            raise ValueError(f"out[{name!r}] must be float32 {tuple(like.shape)}")
+        _check_tensor(f"out[{name!r}]", t, dev)
+    pr, keep = prob.to_c()
+    _check(load_library().polar_attn_bwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g),
+                                         _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out
+
+
 def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_scale=None, out=None,
           stats=False):
     """Merge split statistics (polar_attn_merge): partials [B,H,Tq,S,d+3] fp32 on the GPU."""
@@ -373,6 +438,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["fwd", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

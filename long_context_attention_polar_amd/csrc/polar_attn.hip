@@ -9,6 +9,7 @@
 #include <type_traits>
 
 #include "../../include/polar_attn.h"
+#include "bwd.h"
 #include "decode.h"
 #include "decode_group.h"
 #include "fwd_bf16.h"
@@ -302,6 +303,35 @@ polar_status merge_with_lens(const polar_problem* pr, const float* partials, int
   return pr->head_dim == 64 ? launch_merge<64>(pr, mp, stream) : launch_merge<128>(pr, mp, stream);
 }
 
+// ---- backward
+
+size_t bwd_workspace(const polar_problem* pr) {
+  return (size_t)pr->batch * pr->heads * pr->seq_q * (pr->head_dim + 4) * sizeof(float);
+}
+
+template <int D, typename T, bool CAUSAL>
+polar_status launch_bwd(const polar::BwdParams& bp, void* stream) {
+  constexpr int kRows = polar::kBwdThreads / (D / 32);  // rows (or keys) per workgroup
+  const dim3 block(polar::kBwdThreads);
+  if (bp.Tq > 0) {
+    const dim3 grid((bp.Tq + kRows - 1) / kRows, bp.B * bp.H);
+    polar_status st = launch(polar::polar_bwd_rows_kernel<D, T, CAUSAL>, grid, block, bp, stream);
+    if (st != POLAR_OK) return st;
+    st = launch(polar::polar_bwd_dq_kernel<D, T, CAUSAL>, grid, block, bp, stream);
+    if (st != POLAR_OK) return st;
+  }
+  // with no query rows this writes zero dk and dv
+  const dim3 grid((bp.Tk + kRows - 1) / kRows, bp.B * bp.Hkv);
+  return launch(polar::polar_bwd_dkdv_kernel<D, T, CAUSAL>, grid, block, bp, stream);
+}
+
+template <typename T>
+polar_status dispatch_bwd(const polar_problem* pr, const polar::BwdParams& bp, void* stream) {
+  if (pr->head_dim == 64)
+    return pr->causal ? launch_bwd<64, T, true>(bp, stream) : launch_bwd<64, T, false>(bp, stream);
+  return pr->causal ? launch_bwd<128, T, true>(bp, stream) : launch_bwd<128, T, false>(bp, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -523,6 +553,71 @@ polar_status polar_attn_fwd_partial(const polar_problem* pr, const void* q, cons
   if (pr->head_dim == 64)
     return pr->causal ? launch_fwd<64, true>(pr, fp, stream) : launch_fwd<64, false>(pr, fp, stream);
   return pr->causal ? launch_fwd<128, true>(pr, fp, stream) : launch_fwd<128, false>(pr, fp, stream);
+}
+
+size_t polar_attn_bwd_workspace_bytes(const polar_problem* pr) {
+  bool empty = false;
+  if (check_shape(pr, empty) != POLAR_OK) return 0;
+  return bwd_workspace(pr);
+}
+
+polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* k, const void* v,
+                            const polar_grads* g, float* dq, float* dk, float* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  polar_status st = check_shape(pr, empty);
+  if (st != POLAR_OK) return st;
+  polar::BwdParams bp;
+  std::memset(&bp, 0, sizeof(bp));
+  st = head_params(pr, bp.hp, bp.hp_stride, bp.floor_on, bp.scale);
+  if (st != POLAR_OK) return st;
+  if (!g) return POLAR_ERR_NULL_ARG;
+  if (pr->batch == 0) return POLAR_OK;  // nothing to write
+  // the grid's second dimension holds (batch, head) pairs
+  if ((int64_t)pr->batch * pr->heads > 65535) return POLAR_ERR_UNSUPPORTED;
+  const bool rows = pr->seq_q > 0;
+  const size_t ws = bwd_workspace(pr);
+  if (!k || !v || !dk || !dv) return POLAR_ERR_NULL_ARG;
+  if (rows && (!q || !dq)) return POLAR_ERR_NULL_ARG;
+  if (ws > 0 && !workspace) return POLAR_ERR_WORKSPACE;
+  if (workspace_bytes < ws) return POLAR_ERR_WORKSPACE;
+  const void* a16[] = {q, k, v, dq, dk, dv, workspace, g->d_direction};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return POLAR_ERR_MISALIGNED;
+  if (!aligned(g->d_n_eff, 4) || !aligned(g->d_confidence, 4) || !aligned(g->d_count, 4))
+    return POLAR_ERR_MISALIGNED;
+  const size_t eb = elem_bytes(pr->dtype);
+  const size_t nq = (size_t)pr->batch * pr->heads * pr->seq_q;
+  const size_t nk = (size_t)pr->batch * pr->kv_heads * pr->seq_k;
+  const size_t D = pr->head_dim;
+  const void* ins[7] = {q, k, v, g->d_direction, g->d_n_eff, g->d_confidence, g->d_count};
+  const size_t in_bytes[7] = {nq * D * eb, nk * D * eb, nk * D * eb, nq * D * 4, nq * 4, nq * 4, nq * 4};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_bytes[4] = {nq * D * 4, nk * D * 4, nk * D * 4, ws};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i])) return POLAR_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return POLAR_ERR_ALIAS;
+  }
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.g_dir = g->d_direction;
+  bp.g_neff = g->d_n_eff;
+  bp.g_conf = g->d_confidence;
+  bp.g_count = g->d_count;
+  bp.W = static_cast<float*>(workspace);
+  bp.R = rows ? static_cast<float*>(workspace) + nq * D : nullptr;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.B = pr->batch;
+  bp.H = pr->heads;
+  bp.Hkv = pr->kv_heads;
+  bp.Tq = pr->seq_q;
+  bp.Tk = pr->seq_k;
+  return pr->dtype == POLAR_F32 ? dispatch_bwd<float>(pr, bp, stream) : dispatch_bwd<__bf16>(pr, bp, stream);
 }
 
 }  // extern "C"

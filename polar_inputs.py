@@ -83,6 +83,11 @@ WORKLOADS = {
         decode=True, extra={"block_size": 16},
         description="Polar Attention grouped split-KV decode over a paged cache, bf16, batch 64, 32 query heads "
                     "over 8 KV heads, d=128, 65536 keys per sequence in shuffled 16-row blocks"),
+    "bf16_bwd_b1_h16_kv4_t16384_d128": Workload(
+        "bf16_bwd_b1_h16_kv4_t16384_d128", torch.bfloat16, 1, 16, 4, 16384, 16384, 128, True, 1007,
+        tau_step=0.01, extra={"grad_seed": 1107},
+        description="Polar Attention backward, bf16 inputs, B=1, 16 query heads over 4 KV heads, T=16384, d=128, "
+                    "causal, tau_h = 0.01 h, N(0,1) upstream gradients of all four channels"),
 }
 
 
@@ -138,6 +143,19 @@ def random_qkv(B, H, Hkv, Tq, Tk, d, dtype=torch.bfloat16, seed=0, plant=None):
         else:
             raise ValueError(plant)
     return q, k, v, meta
+
+
+def random_grads(B, H, Tq, d, seed, names=("direction", "n_eff", "confidence", "count")):
+    """Upstream gradients of the four output channels, i.i.d. N(0, 1) fp32 on the host
+    (direction [B,H,Tq,d], the others [B,H,Tq]); only the channels in `names`."""
+    g = torch.Generator().manual_seed(seed)
+    shapes = {"direction": (B, H, Tq, d), "n_eff": (B, H, Tq), "confidence": (B, H, Tq), "count": (B, H, Tq)}
+    out = {}
+    for name in ("direction", "n_eff", "confidence", "count"):
+        x = torch.randn(shapes[name], generator=g, dtype=torch.float32)  # drawn for every name: stable streams
+        if name in names:
+            out[name] = x
+    return out
 
 
 def workload_inputs(w: Workload, device="cpu"):

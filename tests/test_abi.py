@@ -72,13 +72,16 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
         "F(polar_paged_kv, k_pool) F(polar_paged_kv, v_pool) F(polar_paged_kv, block_table)\n"
         "F(polar_paged_kv, seq_lens) F(polar_paged_kv, num_blocks) F(polar_paged_kv, block_size)\n"
         "F(polar_paged_kv, max_blocks)\n"
+        "F(polar_grads, d_direction) F(polar_grads, d_n_eff) F(polar_grads, d_confidence) F(polar_grads, d_count)\n"
         'printf("sizeof polar_problem %zu\\nsizeof polar_outputs %zu\\n", sizeof(polar_problem), sizeof(polar_outputs));\n'
         'printf("sizeof polar_paged_kv %zu\\n", sizeof(polar_paged_kv));\n'
+        'printf("sizeof polar_grads %zu\\n", sizeof(polar_grads));\n'
         "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
-    classes = {"polar_problem": pa.PolarProblem, "polar_outputs": pa.PolarOutputs, "polar_paged_kv": pa.PolarPagedKV}
+    classes = {"polar_problem": pa.PolarProblem, "polar_outputs": pa.PolarOutputs, "polar_paged_kv": pa.PolarPagedKV,
+               "polar_grads": pa.PolarGrads}
     for line in filter(None, lines):
         a, b, c = line.split()
         if a == "sizeof":
@@ -288,6 +291,50 @@ def test_fwd_partial_validation(lib):
     assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, ctypes.c_void_p(FAKE + 4 * (1 << 34) + 2), 2, 0,
                 None) == 5
     assert call(ctypes.byref(pr), fake(1), fake(2), fake(3), 1000, fake(2), 2, 0, None) == 7  # over k
+
+
+def test_bwd_validation(lib):
+    prob = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128)
+    pr, keep = prob.to_c()
+    ws = 2 * 4 * 48 * (128 + 4) * 4
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr)) == ws
+    bad, keep2 = good_problem(head_dim=96).to_c()
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+    g = pa.PolarGrads(fake(20), fake(21), None, fake(22))
+    call = lib.polar_attn_bwd
+
+    def run(q=1, k=2, v=3, grads=g, dq=4, dk=5, dv=6, work=7, nbytes=ws, problem=pr):
+        arg = lambda x: fake(x) if isinstance(x, int) else x
+        gp = None if grads is None else ctypes.byref(grads)
+        return call(ctypes.byref(problem), arg(q), arg(k), arg(v), gp, arg(dq), arg(dk), arg(dv), arg(work), nbytes,
+                    None)
+
+    assert run(problem=bad) == 3
+    assert run(grads=None) == 1
+    for name in ("q", "k", "v", "dq", "dk", "dv"):
+        assert run(**{name: None}) == 1, name
+    assert run(work=None) == 6
+    assert run(nbytes=ws - 1) == 6
+    odd = ctypes.c_void_p(FAKE + 8 * (1 << 34) + 8)  # 8-byte aligned only
+    for name in ("q", "dq", "dk", "work"):
+        assert run(**{name: odd}) == 5, name
+    assert run(grads=pa.PolarGrads(odd, None, None, None)) == 5
+    assert run(grads=pa.PolarGrads(None, ctypes.c_void_p(FAKE + 2), None, None)) == 5
+    assert run(dk=1) == 7                    # dk over q
+    assert run(work=20) == 7                 # workspace over d_direction
+    assert run(dv=5) == 7                    # dv over dk
+    bad_tau, keep3 = good_problem(len_temp=[0.0, -1.0]).to_c()
+    assert run(problem=bad_tau) == 4
+    # no batch: nothing to do, nothing checked past the problem
+    empty, keep4 = good_problem(batch=0).to_c()
+    assert run(problem=empty, q=None, k=None, v=None, dq=None, dk=None, dv=None, work=None, nbytes=0) == 0
+    # no query rows: q, dq and the workspace may be NULL, k, v, dk, dv may not
+    rows0, keep5 = good_problem(seq_q=0).to_c()
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(rows0)) == 0
+    assert run(problem=rows0, dk=None, q=None, dq=None, work=None, nbytes=0) == 1
+    # the (batch, head) grid dimension is limited to 65535 pairs
+    big, keep6 = good_problem(batch=40000, heads=2, kv_heads=2).to_c()
+    assert run(problem=big) == 3
 
 
 def test_python_binding_checks():

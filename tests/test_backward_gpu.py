@@ -1,0 +1,168 @@
+"""GPU parity of the backward (polar_attn_bwd) against the fp64 gradient oracle.
+
+Both sides see the same input values (bf16 inputs widened exactly); the kernels compute
+in fp32, the oracle in fp64.  Metric, per output tensor: max |gpu - oracle| over the
+tensor divided by max |oracle|.  Every output element is an fp32 sum over at most n
+visible terms (keys for dq, query rows times the group for dk and dv) of products whose
+size the largest output bounds, so its error stays within a small multiple of
+n * 2^-24: BWD_TOL = 1e-4 for the cases here (n <= 1200), BWD_TOL_16K = 1e-3 at 16384
+keys.  A tensor whose exact gradient is zero (no upstream gradient reaches it) must come
+back exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_polar_amd as pa
+import polar_inputs as pin
+from oracle import polar_attention_backward
+from tests.parity import to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BWD_TOL = 1e-4
+BWD_TOL_16K = 1e-3
+ALL = ("direction", "n_eff", "confidence", "count")
+
+
+def compare(out, ref, label):
+    errs = {}
+    for key in ("dq", "dk", "dv"):
+        g, r = to_np(out[key]), ref[key]
+        assert g.shape == r.shape, (label, key)
+        assert np.isfinite(g).all(), f"{label} {key} not finite"
+        top = np.abs(r).max() if r.size else 0.0
+        if top == 0.0:
+            assert not np.any(g), f"{label} {key} should be exactly zero"
+            errs[key] = 0.0
+            continue
+        errs[key] = float(np.abs(g - r).max() / top)
+        assert errs[key] <= BWD_TOL, f"{label} {key}: {errs[key]:.3e} > {BWD_TOL:.0e} ({errs})"
+    print(f"[bwd] {label} {errs}", flush=True)
+    return errs
+
+
+def bwd_case(B, H, Hkv, Tq, Tk, d, dtype, causal, seed, tau=None, beta=None, kappa=None, names=ALL, scale=None):
+    label = f"B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} {dtype} causal={causal} grads={names}"
+    print(f"[bwd] {label}", flush=True)
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, Tq, Tk, d, dtype, seed)
+    gr = pin.random_grads(B, H, Tq, d, seed + 7, names)
+    ref = polar_attention_backward(to_np(q), to_np(k), to_np(v), {n: t.double().numpy() for n, t in gr.items()},
+                                   causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa,
+                                   softmax_scale=scale)
+    out = pa.bwd(q.to(DEV), k.to(DEV), v.to(DEV), {n: t.to(DEV) for n, t in gr.items()}, causal=causal,
+                 len_temp=tau, null_bias=beta, count_scale=kappa, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return compare(out, ref, label)
+
+
+TAU4 = [0.05, 0.0, 0.2, 0.1]
+BETA4 = [0.0, -1.0, 1.5, 0.5]
+KAPPA4 = [1.0, 2.0, 0.5, 4.0]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_against_oracle(d, dtype, causal):
+    """Several row blocks and LDS tiles with ragged tails, GQA groups of 2, per-head
+    temperature, floor and saturation."""
+    Tq, Tk = (150, 150) if causal else (70, 201)
+    bwd_case(2, 4, 2, Tq, Tk, d, dtype, causal, seed=500 + d + causal, tau=TAU4, beta=BETA4, kappa=KAPPA4)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_bwd_each_upstream_channel(name):
+    """One upstream gradient at a time, so each term of the row constants dominates its
+    own case."""
+    bwd_case(1, 2, 1, 100, 100, 128, torch.bfloat16, True, seed=520, tau=[0.1, 0.0], beta=[0.5, -0.5],
+             kappa=[1.0, 3.0], names=(name,))
+
+
+def test_bwd_rows_at_end_of_keys_group_of_four():
+    """Causal with fewer query rows than keys (rows aligned to the end), 4 query heads
+    per KV head."""
+    bwd_case(1, 8, 2, 37, 300, 64, torch.float32, True, seed=530, tau=[0.02 * h for h in range(8)],
+             beta=[0.0] * 8)
+
+
+@pytest.mark.parametrize("Tq,Tk,causal", [(1, 1, True), (1, 1, False), (33, 33, True), (1, 77, True), (5, 1, False)])
+def test_bwd_tiny(Tq, Tk, causal):
+    """One key (n_eff = 1, ln n = 0) and one-row problems; the first causal row sees one key."""
+    bwd_case(1, 2, 2, Tq, Tk, 64, torch.float32, causal, seed=540 + Tq + Tk, beta=[0.0, 1.0], kappa=[1.0, 2.0])
+
+
+def test_bwd_explicit_softmax_scale_and_floor_off():
+    bwd_case(1, 2, 1, 64, 96, 128, torch.bfloat16, True, seed=550, tau=[0.1, 0.3], scale=0.3)
+
+
+def test_bwd_constant_confidence_gives_zero():
+    """With the floor off the confidence is the constant 1: its gradient alone gives
+    exactly zero dq, dk, dv."""
+    errs = bwd_case(1, 2, 2, 40, 40, 64, torch.bfloat16, True, seed=560, names=("confidence",))
+    assert errs == {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+
+
+def test_bwd_no_query_rows():
+    """seq_q == 0: dq is empty and dk, dv are written as zeros."""
+    q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(1, 2, 50, 64, device=DEV).to(torch.bfloat16)
+    out = pa.bwd(q, k, k.clone(), {}, causal=False)
+    torch.cuda.synchronize()
+    assert out["dq"].numel() == 0
+    assert torch.all(out["dk"] == 0) and torch.all(out["dv"] == 0)
+
+
+def test_bwd_rejects_bad_gradients():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        pa.bwd(q, q, q, {"n_eff": torch.zeros(1, 2, 7, device=DEV)})
+    with pytest.raises(ValueError):
+        pa.bwd(q, q, q, {"direction": torch.zeros(1, 2, 8, 64, dtype=torch.float64, device=DEV)})
+    with pytest.raises(ValueError):
+        pa.bwd(q, q, q, {"logits": torch.zeros(1, 2, 8, device=DEV)})
+
+
+def test_workload_backward_16k():
+    """The benchmark's backward workload at full size: dq of sampled rows against the
+    oracle (row i alone over its visible keys gives the same dq_i), and two identities
+    of the gradient that hold at any size:
+      sum_j <v_j, dv_j> = 0          (the outputs do not change when all values are scaled)
+      sum_i <q_i, dq_i> = sum_j <k_j, dk_j>  per KV group  (scores are bilinear in q, k)."""
+    w = pin.WORKLOADS["bf16_bwd_b1_h16_kv4_t16384_d128"]
+    print("[bwd] workload", w.name, flush=True)
+    q, k, v, _ = pin.workload_inputs(w, "cpu")
+    gr = pin.random_grads(w.B, w.H, w.Tq, w.d, w.extra["grad_seed"])
+    tau, beta, kappa = w.len_temp(), w.null_bias(), w.count_scale()
+    out = pa.bwd(q.to(DEV), k.to(DEV), v.to(DEV), {n: t.to(DEV) for n, t in gr.items()}, causal=True,
+                 len_temp=tau, null_bias=beta, count_scale=kappa)
+    torch.cuda.synchronize()
+    dq, dk, dv = out["dq"].double().cpu(), out["dk"].double().cpu(), out["dv"].double().cpu()
+    for key, t in out.items():
+        assert torch.isfinite(t).all(), key
+    group = w.H // w.Hkv
+    r = np.random.default_rng(81)
+    for h, i in [(0, 0), (15, w.Tq - 1), (5, 1)] + [(int(a), int(b)) for a, b in
+                                                    zip(r.integers(0, w.H, 6), r.integers(0, w.Tq, 6))]:
+        n = i + 1
+        hk = h // group
+        row = {nm: t[:, h:h + 1, i:i + 1].double().numpy() for nm, t in gr.items()}
+        ref = polar_attention_backward(to_np(q[:, h:h + 1, i:i + 1]), to_np(k[:, hk:hk + 1, :n]),
+                                       to_np(v[:, hk:hk + 1, :n]), row, causal=False, len_temp=[tau[h]],
+                                       null_bias=[beta[h]], count_scale=[kappa[h]])
+        want = ref["dq"][0, 0, 0]
+        got = dq[0, h, i].numpy()
+        err = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
+        print(f"[bwd] workload dq row h={h} i={i}: {err:.2e}", flush=True)
+        assert err <= BWD_TOL_16K, (h, i, err)
+    qd, kd, vd = q.double(), k.double(), v.double()
+    for hk in range(w.Hkv):
+        heads = slice(hk * group, (hk + 1) * group)
+        sv = float((vd[0, hk] * dv[0, hk]).sum())
+        sv_abs = float((vd[0, hk] * dv[0, hk]).abs().sum())
+        assert abs(sv) <= 1e-4 * sv_abs, (hk, sv, sv_abs)
+        lhs = float((qd[0, heads] * dq[0, heads]).sum())
+        rhs = float((kd[0, hk] * dk[0, hk]).sum())
+        scale = float((qd[0, heads] * dq[0, heads]).abs().sum())
+        assert abs(lhs - rhs) <= 1e-4 * scale, (hk, lhs, rhs, scale)

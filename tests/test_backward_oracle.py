@@ -124,3 +124,28 @@ def test_n_eff_is_stationary_at_uniform_logits():
     g = pb_default.polar_attention_backward(q, k, v, gr, causal=True, len_temp=[0.2, 0.0])
     for name in ("dq", "dk", "dv"):
         assert np.abs(g[name]).max() < 1e-12, name
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_invariance_identities(case):
+    """Identities from invariances of the forward, independent of how the gradient is
+    written: scaling every value leaves all outputs unchanged (sum <v, dv> = 0); the
+    scores are bilinear in q and k (sum <q, dq> = sum <k, dk> per KV head); with the
+    floor off, shifting every key by one vector shifts each row's logits by a constant
+    (sum_j dk_j = 0 per KV head)."""
+    B, H, Hkv, Tq, Tk, d, causal, tau, beta, kappa = case
+    q, k, v, gr, _ = case_inputs(B, H, Hkv, Tq, Tk, d, seed=3)
+    g = pb_default.polar_attention_backward(q, k, v, gr, causal=causal, len_temp=tau, null_bias=beta,
+                                            count_scale=kappa)
+    group = H // Hkv
+    for b in range(B):
+        for hk in range(Hkv):
+            heads = slice(hk * group, (hk + 1) * group)
+            assert abs(np.sum(v[b, hk] * g["dv"][b, hk])) <= 1e-10 * np.sum(np.abs(v[b, hk] * g["dv"][b, hk]))
+            lhs = np.sum(q[b, heads] * g["dq"][b, heads])
+            rhs = np.sum(k[b, hk] * g["dk"][b, hk])
+            assert abs(lhs - rhs) <= 1e-10 * np.sum(np.abs(q[b, heads] * g["dq"][b, heads]))
+    g0 = pb_default.polar_attention_backward(q, k, v, gr, causal=causal, len_temp=tau, null_bias=None,
+                                             count_scale=kappa)
+    shift = g0["dk"].sum(axis=2)
+    assert np.abs(shift).max() <= 1e-10 * np.abs(g0["dk"]).sum(axis=2).max()
