@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 4
+#define POLAR_ABI_VERSION 5
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -81,6 +81,69 @@ typedef enum polar_dtype {
   POLAR_F32 = 1               /* fp32 q, k, v; fp32 arithmetic throughout                  */
 } polar_dtype;
 
+/* Reading variants.  The summary names the length temperature, the extreme-value-
+ * corrected null floor, the confidence gate and the saturation without formulas
+ * [ATMA §2.1], and its ablation compares sliding-window attention [ATMA §3.1].  The
+ * definition above is one reading of each (reading R, all fields 0); these select
+ * alternatives.  n below is the row's visible count.
+ *   temperature  POLAR_TEMP_LOG          lam = 1 + tau_h ln n                 (reading R)
+ *                POLAR_TEMP_SSMAX        lam = tau_h ln n      (tau_h >= 0)
+ *                POLAR_TEMP_TRAIN_RATIO  lam = ln n / ln train_len (train_len >= 2; tau unused)
+ *   floor_level  POLAR_LEVEL_GAUSS       l(n) = sqrt(2 ln n)                  (reading R)
+ *                POLAR_LEVEL_GUMBEL2     l(n) = b_n + gamma a_n, the second-order expected
+ *                                        maximum of n standard normals, r = sqrt(2 ln n),
+ *                                        b_n = r - (ln ln n + ln 4 pi) / (2 r), a_n = 1 / r
+ *                POLAR_LEVEL_QNORM       l(n) = sqrt(2 ln n) scaled by sigma_i =
+ *                                        softmax_scale ||q_i||_2 (the spread of the row's
+ *                                        raw logits for unit-variance keys)
+ *                the floor is f_i = lam_i sigma_i l(n_i) + beta_h (sigma_i = 1 unless QNORM;
+ *                l(1) = 0)
+ *   key_floor    POLAR_KEY_FLOOR_NULL    the floor is a null slot in the normaliser (R)
+ *                POLAR_KEY_FLOOR_SOFT    each key's weight is max(e^{s_ij} - e^{f_i}, 0)
+ *                POLAR_KEY_FLOOR_GATE    each key's weight is e^{s_ij} when s_ij > f_i, else 0
+ *                S1, S2 and acc sum the floored weights; confidence = S1 / (S1 + e^{f - m});
+ *                a row with no weight left gets a zero direction and zero n_eff,
+ *                confidence and count.  Needs null_bias (the floor on).
+ *   saturation   POLAR_SAT_LOG           count = conf tanh(ln n_eff / kappa)  (reading R)
+ *                POLAR_SAT_LOG1P         count = conf tanh(ln(1 + n_eff) / kappa)
+ *   window       0 = none; W > 0: key j is visible to row i iff
+ *                i + seq_k - seq_q - W < j <= i + seq_k - seq_q, so n_i = min(W, causal count)
+ *                (prefill needs causal; decode sees the last W keys of each sequence).
+ * Where an entry point does not support a variant it returns POLAR_ERR_UNSUPPORTED;
+ * an enum value out of range is POLAR_ERR_UNSUPPORTED, a negative window or a
+ * train_len < 2 with POLAR_TEMP_TRAIN_RATIO is POLAR_ERR_BAD_PARAM. */
+typedef enum polar_temperature_form {
+  POLAR_TEMP_LOG = 0,
+  POLAR_TEMP_SSMAX = 1,
+  POLAR_TEMP_TRAIN_RATIO = 2
+} polar_temperature_form;
+
+typedef enum polar_floor_level {
+  POLAR_LEVEL_GAUSS = 0,
+  POLAR_LEVEL_GUMBEL2 = 1,
+  POLAR_LEVEL_QNORM = 2
+} polar_floor_level;
+
+typedef enum polar_key_floor {
+  POLAR_KEY_FLOOR_NULL = 0,
+  POLAR_KEY_FLOOR_SOFT = 1,
+  POLAR_KEY_FLOOR_GATE = 2
+} polar_key_floor;
+
+typedef enum polar_saturation {
+  POLAR_SAT_LOG = 0,
+  POLAR_SAT_LOG1P = 1
+} polar_saturation;
+
+typedef struct polar_variant {
+  int32_t temperature;        /* polar_temperature_form                                     */
+  int32_t train_len;          /* L of POLAR_TEMP_TRAIN_RATIO                                 */
+  int32_t floor_level;        /* polar_floor_level                                          */
+  int32_t key_floor;          /* polar_key_floor                                            */
+  int32_t saturation;         /* polar_saturation                                           */
+  int32_t window;             /* sliding window in keys, 0 = none                           */
+} polar_variant;
+
 typedef struct polar_problem {
   int32_t batch;              /* B >= 0                                                     */
   int32_t heads;              /* query heads >= 1                                           */
@@ -94,6 +157,7 @@ typedef struct polar_problem {
   const float* len_temp;      /* HOST [heads] tau_h, NULL = 0; needs 1 + tau_h ln(seq_k) > 0 */
   const float* null_bias;     /* HOST [heads] beta_h (finite), NULL = null floor off        */
   const float* count_scale;   /* HOST [heads] kappa_h > 0, NULL = 1                          */
+  const polar_variant* variant; /* HOST, NULL = reading R (the definition above)             */
 } polar_problem;
 
 typedef struct polar_outputs {

@@ -31,12 +31,44 @@ STATUS_NAMES = ["POLAR_OK", "POLAR_ERR_NULL_ARG", "POLAR_ERR_BAD_SHAPE", "POLAR_
                 "POLAR_ERR_HIP"]
 
 
+class PolarVariant(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_int32), ("train_len", ctypes.c_int32), ("floor_level", ctypes.c_int32),
+                ("key_floor", ctypes.c_int32), ("saturation", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
 class PolarProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("seq_q", ctypes.c_int32), ("seq_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("len_temp", ctypes.POINTER(ctypes.c_float)), ("null_bias", ctypes.POINTER(ctypes.c_float)),
-                ("count_scale", ctypes.POINTER(ctypes.c_float))]
+                ("count_scale", ctypes.POINTER(ctypes.c_float)), ("variant", ctypes.POINTER(PolarVariant))]
+
+
+# Reading variants by name (polar_variant in include/polar_attn.h); a variant is a dict
+# of any of these keys, the missing ones taking the first (default) value.
+VARIANT_CODES = {
+    "temperature": {"log": 0, "ssmax": 1, "train_ratio": 2},
+    "floor_level": {"gauss": 0, "gumbel2": 1, "qnorm": 2},
+    "key_floor": {"null": 0, "soft": 1, "gate": 2},
+    "saturation": {"log": 0, "log1p": 1},
+}
+
+
+def _variant_c(variant):
+    """polar_variant for a dict such as {"key_floor": "soft", "window": 256}, or None."""
+    if not variant:
+        return None
+    unknown = set(variant) - set(VARIANT_CODES) - {"train_len", "window"}
+    if unknown:
+        raise ValueError(f"unknown variant keys {sorted(unknown)}")
+    codes = {}
+    for key, table in VARIANT_CODES.items():
+        name = variant.get(key, next(iter(table)))
+        if name not in table:
+            raise ValueError(f"variant {key}={name!r}; choose from {sorted(table)}")
+        codes[key] = table[name]
+    return PolarVariant(codes["temperature"], int(variant.get("train_len", 2048)), codes["floor_level"],
+                        codes["key_floor"], codes["saturation"], int(variant.get("window", 0)))
 
 
 class PolarOutputs(ctypes.Structure):
@@ -149,14 +181,17 @@ class Problem:
     len_temp: list | None = None
     null_bias: list | None = None
     count_scale: list | None = None
+    variant: dict | None = None
 
     def to_c(self):
         lt, k1 = _float_array(self.len_temp, self.heads)
         nb, k2 = _float_array(self.null_bias, self.heads)
         cs, k3 = _float_array(self.count_scale, self.heads)
+        var = _variant_c(self.variant)
+        vp = ctypes.pointer(var) if var is not None else None
         pr = PolarProblem(self.batch, self.heads, self.kv_heads, self.seq_q, self.seq_k, self.head_dim,
-                          int(bool(self.causal)), self.dtype, self.softmax_scale, lt, nb, cs)
-        return pr, (k1, k2, k3)  # keep the arrays alive during the call
+                          int(bool(self.causal)), self.dtype, self.softmax_scale, lt, nb, cs, vp)
+        return pr, (k1, k2, k3, var)  # keep the arrays alive during the call
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -198,7 +233,8 @@ def _check_tensor(name, t, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def problem_for(q, k, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None):
+def problem_for(q, k, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
+                variant=None):
     B, H, Tq, d = q.shape
     Bk, Hkv, Tk, dk = k.shape
     if Bk != B or dk != d:
@@ -206,16 +242,17 @@ def problem_for(q, k, *, causal=True, len_temp=None, null_bias=None, count_scale
     return Problem(B, H, Hkv, Tq, Tk, d, causal, _dtype_code(q), float(softmax_scale or 0.0),
                    None if len_temp is None else list(len_temp),
                    None if null_bias is None else list(null_bias),
-                   None if count_scale is None else list(count_scale))
+                   None if count_scale is None else list(count_scale), variant)
 
 
 def fwd(q, k, v, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
-        out=None, stats=False):
+        out=None, stats=False, variant=None):
     """Fused Polar Attention forward (polar_attn_fwd).
 
     q [B,H,Tq,d], k and v [B,Hkv,Tk,d] (bf16 or fp32, contiguous, on one GPU).
     Returns a dict with direction [B,H,Tq,d], n_eff, confidence, count [B,H,Tq] (fp32)
-    and stats [B,H,Tq,3] when stats=True.  Work is enqueued on the current stream.
+    and stats [B,H,Tq,3] when stats=True.  `variant`: a reading variant (see
+    VARIANT_CODES), None for the default reading.  Work is enqueued on the current stream.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -223,7 +260,7 @@ def fwd(q, k, v, *, causal=True, len_temp=None, null_bias=None, count_scale=None
     if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k and v must match each other and q's dtype")
     prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
-                       softmax_scale=softmax_scale)
+                       softmax_scale=softmax_scale, variant=variant)
     if out is None:
         out = allocate_outputs(prob.batch, prob.heads, prob.seq_q, prob.head_dim, dev, stats=stats)
     pr, keep = prob.to_c()
@@ -234,7 +271,7 @@ def fwd(q, k, v, *, causal=True, len_temp=None, null_bias=None, count_scale=None
 
 
 def fwd_partial(q, k, v, *, causal=True, context_k=0, partials=None, num_splits=1, split=0, len_temp=None,
-                null_bias=None, count_scale=None, softmax_scale=None):
+                null_bias=None, count_scale=None, softmax_scale=None, variant=None):
     """Partial forward (polar_attn_fwd_partial): writes the (m, S1, S2, acc) rows of this
     call's keys into slot `split` of partials [B,H,Tq,num_splits,d+3] fp32 (allocated, with
     m = -inf everywhere, when not given) and returns it.  context_k: keys of the whole
@@ -245,7 +282,7 @@ def fwd_partial(q, k, v, *, causal=True, context_k=0, partials=None, num_splits=
     if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k and v must match each other and q's dtype")
     prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
-                       softmax_scale=softmax_scale)
+                       softmax_scale=softmax_scale, variant=variant)
     shape = (prob.batch, prob.heads, prob.seq_q, num_splits, prob.head_dim + 3)
     if partials is None:
         partials = torch.zeros(shape, dtype=torch.float32, device=dev)
@@ -270,7 +307,7 @@ def decode_workspace_bytes(prob: Problem, num_splits: int = 0) -> int:
 
 
 def decode(q, k_cache, v_cache, *, num_splits=0, len_temp=None, null_bias=None, count_scale=None,
-           softmax_scale=None, workspace=None, out=None, stats=False):
+           softmax_scale=None, workspace=None, out=None, stats=False, variant=None):
     """Split-KV decode (polar_attn_decode): q [B,H,1,d] against caches [B,Hkv,Tk,d], bf16.
 
     Returns the same dict as fwd(); `workspace` (a uint8 device tensor) is allocated
@@ -279,7 +316,7 @@ def decode(q, k_cache, v_cache, *, num_splits=0, len_temp=None, null_bias=None, 
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(name, t, dev)
     prob = problem_for(q, k_cache, causal=True, len_temp=len_temp, null_bias=null_bias,
-                       count_scale=count_scale, softmax_scale=softmax_scale)
+                       count_scale=count_scale, softmax_scale=softmax_scale, variant=variant)
     lib = load_library()
     pr, keep = prob.to_c()
     splits = int(lib.polar_attn_decode_num_splits(ctypes.byref(pr), num_splits))
@@ -326,7 +363,8 @@ def decode_paged_workspace_bytes(prob: Problem, kv: PolarPagedKV, num_splits: in
 
 
 def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, seq_k=None, num_splits=0, len_temp=None,
-                 null_bias=None, count_scale=None, softmax_scale=None, workspace=None, out=None, stats=False):
+                 null_bias=None, count_scale=None, softmax_scale=None, workspace=None, out=None, stats=False,
+                 variant=None):
     """Grouped split-KV decode over a paged cache (polar_attn_decode_paged).
 
     q [B,H,1,d] bf16; pools [num_blocks, block_size, Hkv, d] bf16; block_table [B, max_blocks]
@@ -344,7 +382,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, seq_k=None, num_sp
     prob = Problem(B, H, Hkv, Tq, int(seq_k), d, False, _dtype_code(q), float(softmax_scale or 0.0),
                    None if len_temp is None else list(len_temp),
                    None if null_bias is None else list(null_bias),
-                   None if count_scale is None else list(count_scale))
+                   None if count_scale is None else list(count_scale), variant)
     lib = load_library()
     pr, keep = prob.to_c()
     splits = int(lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), num_splits))
@@ -372,7 +410,7 @@ def bwd_workspace_bytes(prob: Problem) -> int:
 
 
 def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
-        workspace=None, out=None):
+        workspace=None, out=None, variant=None):
     """Backward of the forward (polar_attn_bwd): gradients of
     sum(grads["direction"] * direction) + sum(grads["n_eff"] * n_eff) + ... with respect to
     q, k, v.  grads maps any of "direction" [B,H,Tq,d], "n_eff", "confidence", "count"
@@ -387,7 +425,7 @@ def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_sca
     if unknown:
         raise ValueError(f"unknown gradient names {sorted(unknown)}")
     prob = problem_for(q, k, causal=causal, len_temp=len_temp, null_bias=null_bias, count_scale=count_scale,
-                       softmax_scale=softmax_scale)
+                       softmax_scale=softmax_scale, variant=variant)
     row_shape = (prob.batch, prob.heads, prob.seq_q)
     for name in GRAD_NAMES:
         t = grads.get(name)
@@ -418,7 +456,7 @@ def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_sca
 
 
 def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_scale=None, out=None,
-          stats=False):
+          stats=False, variant=None):
     """Merge split statistics (polar_attn_merge): partials [B,H,Tq,S,d+3] fp32 on the GPU."""
     dev = partials.device
     _check_tensor("partials", partials, dev)
@@ -429,7 +467,7 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     prob = Problem(B, H, H, Tq, seq_k, d, causal, POLAR_BF16, 0.0,
                    None if len_temp is None else list(len_temp),
                    None if null_bias is None else list(null_bias),
-                   None if count_scale is None else list(count_scale))
+                   None if count_scale is None else list(count_scale), variant)
     if out is None:
         out = allocate_outputs(B, H, Tq, d, dev, stats=stats)
     pr, keep = prob.to_c()
@@ -438,6 +476,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["PolarVariant", "VARIANT_CODES", "fwd", "bwd", "bwd_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

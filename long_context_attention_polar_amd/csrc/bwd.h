@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kBwdThreads) void polar_bwd_rows_kernel(const BwdPa
   const size_t ri = (size_t)bh * Tq + rc;
   const int hpi = h * p.hp_stride;
   const int n = visible_keys(rc, Tq, Tk, CAUSAL);
-  const float lam = length_temperature(p.hp.tau[hpi], n);
+  const float lam = row_temperature(p.hp, hpi, n);
   const float c = lam * p.scale * kLog2e;
   const int kmax = CAUSAL ? rc + off : Tk - 1;  // last visible key
   const T* kb = (const T*)p.k + (size_t)(b * p.Hkv + hk) * Tk * D;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kBwdThreads) void polar_bwd_rows_kernel(const BwdPa
     const float n_eff = s1 * s1 / s2;
     float conf = 1.0f, dconf = 0.0f;
     if (p.floor_on) {
-      const float f = lam * sqrtf(2.0f * logf((float)n)) + p.hp.beta[hpi];
+      const float f = null_floor(p.hp, hpi, n, lam, 1.0f);
       conf = 1.0f / (1.0f + expf(f - m * kLn2 - logf(s1)));
       dconf = conf * (1.0f - conf);
     }

@@ -10,6 +10,11 @@
 // Inside a split workgroup (NW waves), LPK = D / 8 lanes share one key (8 dims each) and
 // each group of LPK lanes is a "slot" with its own running state; slots are combined
 // through LDS at the end of the split.
+//
+// Reading variants: a sliding window moves split 0 to the window's first key; a per-key
+// floor reduces each weight against the floor of the query's whole visible count (the
+// floored weights are linear in e^s - e^f, so the merge is unchanged).  The floor is the
+// template flag KF, so the default kernel carries no floor code.
 #pragma once
 
 #include "polar_common.h"
@@ -35,7 +40,7 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-template <int D, int NW, int UNROLL>
+template <int D, int NW, int UNROLL, int KF = POLAR_KEY_FLOOR_NULL>
 __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const DecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;       // keys per wave per step
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
   const int b = blockIdx.z;
   const int hk = h / (p.H / p.Hkv);
   const int Tk = p.Tk;
-  const int lo = s * p.split_len;
+  const int lo = p.key0 + s * p.split_len;
   const int hi = min(lo + p.split_len, Tk);
 
   const __bf16* qp = (const __bf16*)p.q + ((size_t)b * p.H + h) * D;
@@ -65,9 +70,11 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
   const __bf16* vb = (const __bf16*)p.v + ((size_t)b * p.Hkv + hk) * Tk * D;
 
   const int hpi = h * p.hp_stride;
-  // One query per sequence: it sees every cached key, n = Tk (never a per-split count).
-  const float lam = length_temperature(p.hp.tau[hpi], Tk);
-  const float c = lam * p.scale * kLog2e;
+  // One query per sequence: it sees every cached key (or the last `window` of them),
+  // n = Tk - key0, never a per-split count.
+  const int n = Tk - p.key0;
+  const float lam = row_temperature(p.hp, hpi, n);
+  const float c = logit_scale(lam, p.scale);
 
   float qv[8];
   {
@@ -77,6 +84,16 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
       qv[2 * e] = bf16_lo(w[e]);
       qv[2 * e + 1] = bf16_hi(w[e]);
     }
+  }
+  // per-key floor: the query's floor in base-2 units
+  float f2 = 0.0f;
+  if constexpr (KF != POLAR_KEY_FLOOR_NULL) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qq = fmaf(qv[e], qv[e], qq);
+    qq = group_sum<LPK>(qq);
+    const float sigma = p.hp.level_form == POLAR_LEVEL_QNORM ? p.scale * sqrtf(qq) : 1.0f;
+    f2 = null_floor(p.hp, hpi, n, lam, sigma) * kLog2e;
   }
 
   float m = kMaxInit, s1 = 0.0f, s2 = 0.0f;
@@ -119,9 +136,13 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     m = m_new;
+    // the floor's weight (inf while m is far below the floor: every weight is then 0)
+    const float phi = KF == POLAR_KEY_FLOOR_SOFT ? fast_exp2(f2 - m) : 0.0f;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const float pv = fast_exp2(x[u] - m);
+      float pv = fast_exp2(x[u] - m);
+      if constexpr (KF == POLAR_KEY_FLOOR_SOFT) pv = fmaxf(pv - phi, 0.0f);
+      if constexpr (KF == POLAR_KEY_FLOOR_GATE) pv = x[u] > f2 ? pv : 0.0f;
       s1 += pv;
       s2 = fmaf(pv, pv, s2);
 #pragma unroll
@@ -201,14 +222,29 @@ __global__ __launch_bounds__(64) void polar_merge_kernel(const MergeParams p) {
   const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) p.dir[row * D + lane + 64 * e] = acc[e] * inv;
+  // the data-adaptive floor level needs the norm of the row's q (all lanes take part)
+  float sigma = 1.0f;
+  if (p.hp.level_form == POLAR_LEVEL_QNORM && p.q) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float x = (float)p.q[row * D + lane + 64 * e];
+      qq = fmaf(x, x, qq);
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) qq += __shfl_xor(qq, sh, 64);
+    sigma = p.scale * sqrtf(qq);
+  }
   if (lane == 0) {
     const int hpi = h * p.hp_stride;
     int n = visible_keys(i, p.Tq, p.Tk, p.causal != 0);
     if (p.lens) n = min(max(p.lens[row / ((size_t)p.H * p.Tq)], 0), p.Tk);
+    if (p.hp.window > 0) n = min(n, p.hp.window);
     float neff = 0.0f, conf = 0.0f, count = 0.0f;
     if (n > 0 && M > -INFINITY) {
-      const float lam = length_temperature(p.hp.tau[hpi], n);
-      magnitude_channel(M, S1, S2, n, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf, count);
+      const float lam = row_temperature(p.hp, hpi, n);
+      const float f = null_floor(p.hp, hpi, n, lam, sigma);
+      magnitude_channel(p.hp, hpi, M, S1, S2, f, p.floor_on != 0, neff, conf, count);
     }  // a row that saw no key: direction 0 and all channels 0
     p.neff[row] = neff;
     if (p.conf) p.conf[row] = conf;

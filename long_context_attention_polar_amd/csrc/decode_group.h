@@ -17,6 +17,11 @@
 //
 // The arithmetic of a query does not depend on whether the cache is paged (only the row
 // address differs), so paged and contiguous runs give bitwise-equal partials.
+//
+// Reading variants: a sliding window keeps the last `window` keys of each sequence (the
+// splits cover [len - window, len)); a per-key floor reduces each weight against the
+// floor of the query's visible count (the template flag KF, so the default kernels carry
+// no floor code).
 #pragma once
 
 #include "decode.h"
@@ -42,7 +47,7 @@ struct GroupDecodeParams {
   HeadParams hp;
 };
 
-template <int D, int G, int NW, int UNROLL, bool PAGED>
+template <int D, int G, int NW, int UNROLL, bool PAGED, int KF = POLAR_KEY_FLOOR_NULL>
 __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const GroupDecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key (8 dims each)
   constexpr int KPW = 64 / LPK;       // keys per wave per step
@@ -65,19 +70,36 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const Group
   const int b = blockIdx.z;
   int len = p.Tk;
   if constexpr (PAGED) len = min(max(p.lens[b], 0), p.Tk);
-  const int lo = s * p.split_len;
+  const int start = p.hp.window > 0 ? max(0, len - p.hp.window) : 0;  // first key of the window
+  const int lo = start + s * p.split_len;
   const int hi = min(lo + p.split_len, len);
+  const int n = max(len - start, 1);
 
-  // One query per sequence; it sees every cached key of its sequence, n = len (never a
-  // per-split count).
+  // One query per sequence; it sees every cached key of its sequence (or the last
+  // `window` of them), n = len - start (never a per-split count).
   uint32_t qw[G][4];
-  float c[G];
+  float c[G], f2[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const u32x4 w = *(const u32x4*)((const __bf16*)p.q + ((size_t)b * p.H + h0 + g) * D + dch * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qw[g][e] = w[e];
-    c[g] = length_temperature(p.hp.tau[(h0 + g) * p.hp_stride], max(len, 1)) * p.scale * kLog2e;
+    const int hpi = (h0 + g) * p.hp_stride;
+    const float lam = row_temperature(p.hp, hpi, n);
+    c[g] = logit_scale(lam, p.scale);
+    f2[g] = 0.0f;
+    if constexpr (KF != POLAR_KEY_FLOOR_NULL) {
+      float qq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = qw[g][e];
+        qq = fmaf(bf16_lo(x), bf16_lo(x), qq);
+        qq = fmaf(bf16_hi(x), bf16_hi(x), qq);
+      }
+      qq = group_sum<LPK>(qq);
+      const float sigma = p.hp.level_form == POLAR_LEVEL_QNORM ? p.scale * sqrtf(qq) : 1.0f;
+      f2[g] = null_floor(p.hp, hpi, n, lam, sigma) * kLog2e;
+    }
   }
 
   // address of the 16-byte chunk of key `key` (valid keys only)
@@ -155,9 +177,13 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const Group
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
       m[g] = m_new;
+      // the floor's weight (inf while m is far below the floor: every weight is then 0)
+      const float phi = KF == POLAR_KEY_FLOOR_SOFT ? fast_exp2(f2[g] - m[g]) : 0.0f;
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const float pv = fast_exp2(x[u] - m[g]);
+        float pv = fast_exp2(x[u] - m[g]);
+        if constexpr (KF == POLAR_KEY_FLOOR_SOFT) pv = fmaxf(pv - phi, 0.0f);
+        if constexpr (KF == POLAR_KEY_FLOOR_GATE) pv = x[u] > f2[g] ? pv : 0.0f;
         s1[g] += pv;
         s2[g] = fmaf(pv, pv, s2[g]);
 #pragma unroll

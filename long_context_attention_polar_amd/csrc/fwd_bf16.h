@@ -34,6 +34,11 @@
 //   * sum p and sum p^2 are taken from the same bf16-rounded weights that enter P V, two
 //     at a time with v_dot2_f32_bf16 (exact products, fp32 sums), as per-lane partial
 //     sums combined once in the epilogue.
+//   * Reading variants that change the inner loop are template flags: KF, a per-key
+//     floor (1: weight max(e^s - e^f, 0); 2: e^s only when s > f), for which a row's
+//     reference starts at its floor f so the floor's own weight e^{f - m_ref} never
+//     exceeds 1; WIN, a sliding window, which skips the tiles before a workgroup's
+//     window and masks the tiles it starts in.
 #pragma once
 
 #ifndef POLAR_SCHED_HINTS
@@ -101,10 +106,12 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int kv0, 
   }
 }
 
-template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL, bool STATS>
+template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL, bool STATS, int KF = POLAR_KEY_FLOOR_NULL,
+          bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_fwd_bf16_kernel(
     const FwdParams p) {
   static_assert(BN == 32 || BN == 64, "key tile");
+  static_assert(!WIN || CAUSAL, "a sliding window needs the causal alignment");
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(NB == 1 || NB == 2, "query blocks per wave");
   constexpr int QPW = 32 * NB;  // query rows per wave
@@ -149,22 +156,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   // last key any row of the wave may see, and the smallest such limit over its rows
   const int wave_kmax = CAUSAL ? min(wq0 + QPW - 1 + off, Tk - 1) : Tk - 1;
   const int wave_kmin = CAUSAL ? min(wq0 + off, Tk - 1) : Tk - 1;
+  // sliding window: row i sees keys from i + off - win + 1; the first tile of the
+  // workgroup, and the smallest and largest first key over the wave's rows
+  const int win = WIN ? p.hp.window : 0;
+  const int t_begin = WIN ? max(0, q0 + off - win + 1) / BN : 0;
+  const int wave_klo_min = wq0 + off - win + 1;
+  const int wave_klo_max = wq0 + QPW - 1 + off - win + 1;
 
   // Start the first tile's loads before anything else.
-  load_tile<D, BN, NW>(kb, 0, voff, k_buf0, wave);
-  load_tile<D, BN, NW>(vb, 0, voff, v_buf0, wave);
+  load_tile<D, BN, NW>(kb, t_begin * BN, voff, k_buf0, wave);
+  load_tile<D, BN, NW>(vb, t_begin * BN, voff, v_buf0, wave);
 
-  // a1: per query block: row, visible count, temperature, base-2 logit scale, mask limit
+  // a1: per query block: row, visible count, temperature, base-2 logit scale, mask limits
   const int hpi = h * p.hp_stride;
-  int qrow[NB], n_vis[NB], kmax[NB];
+  int qrow[NB], n_vis[NB], kmax[NB], klo[NB];
   float lam[NB], c[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     qrow[nb] = wq0 + nb * 32 + col;
     n_vis[nb] = context_count(qrow[nb], Tq, Tk, CAUSAL, p.ctx_k);
-    lam[nb] = length_temperature(p.hp.tau[hpi], n_vis[nb]);
-    c[nb] = lam[nb] * p.scale * kLog2e;
+    if (WIN) n_vis[nb] = min(n_vis[nb], win);
+    lam[nb] = row_temperature(p.hp, hpi, n_vis[nb]);
+    c[nb] = logit_scale(lam[nb], p.scale);
     kmax[nb] = CAUSAL ? min(qrow[nb] + off, Tk - 1) : Tk - 1;
+    klo[nb] = WIN ? qrow[nb] + off - win + 1 : 0;
   }
 
   // Q^T fragments: lane holds query qrow[nb], dims ks*16 + 8*half + [0, 8).
@@ -205,13 +220,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     }
   }
 
+  // per-key floor: the row's floor f in base-2 units (the data-adaptive level needs the
+  // norm of q, whose halves sit in lanes l and l ^ 32)
+  float f2[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) f2[nb] = 0.0f;
+  if constexpr (KF != POLAR_KEY_FLOOR_NULL) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float qq = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qq = fmaf((float)qf[nb][ks][e], (float)qf[nb][ks][e], qq);
+      qq += xor32(qq);
+      const float sigma = p.hp.level_form == POLAR_LEVEL_QNORM ? p.scale * sqrtf(qq) : 1.0f;
+      f2[nb] = null_floor(p.hp, hpi, n_vis[nb], lam[nb], sigma) * kLog2e;
+    }
+  }
+
   // running statistics (base 2), per lane and query block; each row is split over the
   // two lanes l and l ^ 32
   float m_ref[NB], t_max[NB], s1[NB][2], s2[NB][2];
   f32x16 o[NB][DM];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m_ref[nb] = kMaxInit;   // the reference maximum the sums are relative to
+    // the reference maximum the sums are relative to; with a per-key floor it starts at
+    // the floor, so e^{f - m_ref} <= 1 throughout
+    m_ref[nb] = KF != POLAR_KEY_FLOOR_NULL ? f2[nb] : kMaxInit;
     t_max[nb] = -INFINITY;  // true maximum of this lane's raw scores
     s1[nb][0] = s1[nb][1] = s2[nb][0] = s2[nb][1] = 0.0f;
 #pragma unroll
@@ -239,18 +275,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], s[nb][mb], 0, 0, 0);
       }
     bf16x8 pf[NB][PS];
-    // ---- mask on the diagonal / tail tiles only (in place)
-    if (kv0 + BN - 1 > wave_kmin) {
+    // ---- mask on the diagonal / tail tiles (and the window's first tiles) only (in place)
+    if (kv0 + BN - 1 > wave_kmin || (WIN && kv0 < wave_klo_max)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int lim = kmax[nb] - kv0 - 4 * half;  // key offset limit for this lane
+        const int lim = kmax[nb] - kv0 - 4 * half;    // key offset limits for this lane
+        const int lim_lo = klo[nb] - kv0 - 4 * half;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (mb * 32 + 8 * i + j > lim) s[nb][mb][4 * i + j] = -INFINITY;
+            for (int j = 0; j < 4; ++j) {
+              const int r = mb * 32 + 8 * i + j;
+              if (r > lim || (WIN && r < lim_lo)) s[nb][mb][4 * i + j] = -INFINITY;
+            }
       }
     }
     // ---- a5: p = exp2(c s - m_ref) rounded to bf16 in the B-operand order; the tile's sum p
@@ -261,6 +300,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float neg_m = -m_ref[nb];
+        // per-key floor: the floor's weight e^{f - m_ref} (soft), or its offset f - m_ref (gate)
+        const float fl = KF == POLAR_KEY_FLOOR_SOFT ? fast_exp2(f2[nb] - m_ref[nb]) : f2[nb] - m_ref[nb];
+        auto weight = [&](float sc) __attribute__((always_inline)) {
+          const float t = fmaf(c[nb], sc, neg_m);
+          if constexpr (KF == POLAR_KEY_FLOOR_SOFT) return fmaxf(fast_exp2(t) - fl, 0.0f);
+          if constexpr (KF == POLAR_KEY_FLOOR_GATE) return t > fl ? fast_exp2(t) : 0.0f;
+          return fast_exp2(t);
+        };
         float a1[2] = {0.0f, 0.0f}, a2[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -269,8 +316,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
             for (int j = 0; j < 4; j += 2) {
               bf16x2 pp;
-              pp[0] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j], neg_m));
-              pp[1] = (__bf16)fast_exp2(fmaf(c[nb], s[nb][mb][4 * i + j + 1], neg_m));
+              pp[0] = (__bf16)weight(s[nb][mb][4 * i + j]);
+              pp[1] = (__bf16)weight(s[nb][mb][4 * i + j + 1]);
               a1[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, a1[j >> 1], false);
               a2[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, a2[j >> 1], false);
               pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
@@ -345,21 +392,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
       }
   };
 
+  // a tile the wave needs: not past its last visible key, not before its window
+  auto wave_needs = [&](int kv0) __attribute__((always_inline)) {
+    return kv0 <= wave_kmax && (!WIN || kv0 + BN - 1 >= wave_klo_min);
+  };
+
   // ---- main loop: tile t is read from one buffer pair while tile t+1 loads into the other
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_begin; t < ntiles; t += 2) {
     if (t + 1 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 1) * BN, voff, k_buf1, wave);
       load_tile<D, BN, NW>(vb, (t + 1) * BN, voff, v_buf1, wave);
     }
-    if (t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
+    if (wave_needs(t * BN)) compute_tile(k_buf0, v_buf0, t * BN);
     __syncthreads();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 2) * BN, voff, k_buf0, wave);
       load_tile<D, BN, NW>(vb, (t + 2) * BN, voff, v_buf0, wave);
     }
-    if ((t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
+    if (wave_needs((t + 1) * BN)) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
     __syncthreads();
   }
 
@@ -381,11 +433,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
       for (int e = 0; e < 16; ++e) nn = fmaf(o[nb][dm][e], o[nb][dm][e], nn);
     nn += xor32(nn);
     const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+    // the data-adaptive floor level needs the norm of the row's q (all lanes take part)
+    float sigma = 1.0f;
+    if (p.hp.level_form == POLAR_LEVEL_QNORM) {
+      float qq = 0.0f;
+      if (qrow[nb] < Tq) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 x = *(const bf16x8*)(qb + (size_t)qrow[nb] * D + ks * 16 + 8 * half);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qq = fmaf((float)x[e], (float)x[e], qq);
+        }
+      }
+      qq += xor32(qq);
+      sigma = p.scale * sqrtf(qq);
+    }
     if (STATS && p.part) {
       // partial mode: the statistics of this call's keys relative to their true maximum
       if (qrow[nb] < Tq) {
         const float m_true = c[nb] * row_tmax;
-        const float to_true = fast_exp2(m_ref[nb] - m_true);
+        // with a per-key floor the reference may sit above the true maximum; the sums are
+        // then 0 (no key above the floor) and must not meet an overflowing factor
+        const float to_true = S1 > 0.0f ? fast_exp2(m_ref[nb] - m_true) : 0.0f;
         const size_t row = (size_t)bh * Tq + qrow[nb];
         float* out = p.part + (row * p.part_S + p.part_s) * (D + 3);
 #pragma unroll
@@ -415,14 +484,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         }
       if (half == 0) {
         float neff, conf, count;
-        magnitude_channel(m_ref[nb] * kLn2, S1, S2, n_vis[nb], lam[nb], p.floor_on != 0, p.hp.beta[hpi],
-                          p.hp.kinv[hpi], neff, conf, count);
+        const float f = null_floor(p.hp, hpi, n_vis[nb], lam[nb], sigma);
+        magnitude_channel(p.hp, hpi, m_ref[nb] * kLn2, S1, S2, f, p.floor_on != 0, neff, conf, count);
         p.neff[row] = neff;
         if (p.conf) p.conf[row] = conf;
         if (p.count) p.count[row] = count;
         if (STATS && p.stats) {
           const float m_true = c[nb] * row_tmax;
-          const float to_true = fast_exp2(m_ref[nb] - m_true);
+          const float to_true = S1 > 0.0f ? fast_exp2(m_ref[nb] - m_true) : 0.0f;
           p.stats[row * 3 + 0] = m_true * kLn2;
           p.stats[row * 3 + 1] = S1 * to_true;
           p.stats[row * 3 + 2] = S2 * to_true * to_true;

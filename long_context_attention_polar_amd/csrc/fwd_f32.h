@@ -4,7 +4,9 @@
 // VALU FMAs: one thread per query row, K and V tiles of BK keys staged in LDS and read
 // by every thread of the workgroup as broadcasts.  The statistics follow the same
 // streaming algebra as the bf16 kernel [ATMA §2.2, fused kernel]: a move of the
-// reference maximum rescales sum p and acc by alpha and sum p^2 by alpha^2.
+// reference maximum rescales sum p and acc by alpha and sum p^2 by alpha^2.  The reading
+// variants (per-key floor, sliding window) are runtime choices here: this path is not
+// the throughput path, and every branch on them is uniform over the workgroup.
 #pragma once
 
 #include "polar_common.h"
@@ -35,10 +37,14 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
   const float* vb = (const float*)p.v + (size_t)(b * p.Hkv + hk) * Tk * D;
 
   const int hpi = h * p.hp_stride;
-  const int n_vis = context_count(qrow, Tq, Tk, CAUSAL, p.ctx_k);
-  const float lam = length_temperature(p.hp.tau[hpi], n_vis);
-  const float c = lam * p.scale * kLog2e;
+  const int win = CAUSAL ? p.hp.window : 0;
+  int n_vis = context_count(qrow, Tq, Tk, CAUSAL, p.ctx_k);
+  if (win > 0) n_vis = min(n_vis, win);
+  const float lam = row_temperature(p.hp, hpi, n_vis);
+  const float c = logit_scale(lam, p.scale);
   const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
+  const int klo = win > 0 ? qrow + off - win + 1 : 0;  // first key of the row's window
+  const int kf = p.hp.key_floor;
 
   float q[D];
 #pragma unroll
@@ -49,13 +55,21 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
     q[e + 2] = x[2];
     q[e + 3] = x[3];
   }
+  float qq = 0.0f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) qq = fmaf(q[e], q[e], qq);
+  const float sigma = p.hp.level_form == POLAR_LEVEL_QNORM ? p.scale * sqrtf(qq) : 1.0f;
+  const float f = null_floor(p.hp, hpi, n_vis, lam, sigma);  // the row's floor (natural units)
+  const float f2 = f * kLog2e;
   float acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.0f;
-  float m_ref = kMaxInit, m_true = kMaxInit, s1 = 0.0f, s2 = 0.0f;
+  // with a per-key floor the reference starts at the floor, so e^{f - m_ref} <= 1
+  float m_ref = kf != POLAR_KEY_FLOOR_NULL ? f2 : kMaxInit, m_true = kMaxInit, s1 = 0.0f, s2 = 0.0f;
 
   const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += BK) {
+  const int kv_begin = win > 0 ? max(0, q0 + off - win + 1) / BK * BK : 0;
+  for (int kv0 = kv_begin; kv0 < kv_end; kv0 += BK) {
     __syncthreads();
     for (int idx = tid * 4; idx < BK * D; idx += NT * 4) {
       const int key = kv0 + idx / D;
@@ -72,7 +86,7 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
       float r = 0.0f;
 #pragma unroll
       for (int e = 0; e < D; ++e) r = fmaf(q[e], k_lds[j * D + e], r);
-      sc[j] = (kv0 + j <= kmax) ? r : -INFINITY;
+      sc[j] = (kv0 + j <= kmax && kv0 + j >= klo) ? r : -INFINITY;
       tmax = fmaxf(tmax, sc[j]);
     }
     const float cm = c * tmax;
@@ -86,9 +100,15 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
       for (int e = 0; e < D; ++e) acc[e] *= alpha;
       m_ref = m_new;
     }
+    const float phi = fast_exp2(f2 - m_ref);  // the floor's weight, for the soft per-key floor
 #pragma unroll
     for (int j = 0; j < BK; ++j) {
-      const float pv = fast_exp2(fmaf(c, sc[j], -m_ref));
+      const float x = c * sc[j];
+      float pv = fast_exp2(x - m_ref);
+      // soft floor: e^s - e^f = e^f (e^{s - f} - 1), with expm1 so that a score just above
+      // the floor keeps its relative precision
+      if (kf == POLAR_KEY_FLOOR_SOFT) pv = x > f2 ? phi * expm1f((x - f2) * kLn2) : 0.0f;
+      if (kf == POLAR_KEY_FLOOR_GATE) pv = x > f2 ? pv : 0.0f;
       s1 += pv;
       s2 = fmaf(pv, pv, s2);
 #pragma unroll
@@ -96,9 +116,11 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
     }
   }
 
+  // with a per-key floor the reference may sit above the true maximum; the sums are then
+  // 0 and must not meet an overflowing factor
+  const float to_true = s1 > 0.0f ? fast_exp2(m_ref - m_true) : 0.0f;
   if (qrow < Tq && p.part) {
     // partial mode: the statistics of this call's keys relative to their true maximum
-    const float to_true = fast_exp2(m_ref - m_true);
     float* out = p.part + (((size_t)bh * Tq + qrow) * p.part_S + p.part_s) * (D + 3);
     out[0] = m_true * kLn2;
     out[1] = s1 * to_true;
@@ -106,7 +128,6 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
 #pragma unroll
     for (int e = 0; e < D; ++e) out[3 + e] = acc[e] * to_true;
   } else if (qrow < Tq) {
-    const float to_true = fast_exp2(m_ref - m_true);
     const float S1 = s1 * to_true;
     const float S2 = s2 * to_true * to_true;
     float nn = 0.0f;
@@ -122,8 +143,7 @@ __global__ __launch_bounds__(128) void polar_fwd_f32_kernel(const FwdParams p) {
     }
     const float m_nat = m_true * kLn2;
     float neff, conf, count;
-    magnitude_channel(m_nat, S1, S2, n_vis, lam, p.floor_on != 0, p.hp.beta[hpi], p.hp.kinv[hpi], neff, conf,
-                      count);
+    magnitude_channel(p.hp, hpi, m_nat, S1, S2, f, p.floor_on != 0, neff, conf, count);
     p.neff[row] = neff;
     if (p.conf) p.conf[row] = conf;
     if (p.count) p.count[row] = count;

@@ -81,10 +81,41 @@ polar_status check_shape(const polar_problem* pr, bool& empty) {
   return POLAR_OK;
 }
 
+// Reading variant -> kernel constants, with the checks every entry point shares.
+polar_status variant_params(const polar_problem* pr, HeadParams& hp) {
+  const polar_variant* v = pr->variant;
+  hp.lam_form = v ? v->temperature : POLAR_TEMP_LOG;
+  hp.level_form = v ? v->floor_level : POLAR_LEVEL_GAUSS;
+  hp.key_floor = v ? v->key_floor : POLAR_KEY_FLOOR_NULL;
+  hp.sat_form = v ? v->saturation : POLAR_SAT_LOG;
+  hp.window = v ? v->window : 0;
+  hp.inv_ln_train = 0.0f;
+  if (hp.lam_form < POLAR_TEMP_LOG || hp.lam_form > POLAR_TEMP_TRAIN_RATIO || hp.level_form < POLAR_LEVEL_GAUSS ||
+      hp.level_form > POLAR_LEVEL_QNORM || hp.key_floor < POLAR_KEY_FLOOR_NULL ||
+      hp.key_floor > POLAR_KEY_FLOOR_GATE || hp.sat_form < POLAR_SAT_LOG || hp.sat_form > POLAR_SAT_LOG1P)
+    return POLAR_ERR_UNSUPPORTED;
+  if (hp.window < 0) return POLAR_ERR_BAD_PARAM;
+  if (hp.lam_form == POLAR_TEMP_TRAIN_RATIO) {
+    if (v->train_len < 2) return POLAR_ERR_BAD_PARAM;
+    hp.inv_ln_train = (float)(1.0 / std::log((double)v->train_len));
+  }
+  // a per-key floor needs a floor
+  if (hp.key_floor != POLAR_KEY_FLOOR_NULL && !pr->null_bias) return POLAR_ERR_BAD_PARAM;
+  return POLAR_OK;
+}
+
+bool default_variant(const HeadParams& hp) {
+  return hp.lam_form == POLAR_TEMP_LOG && hp.level_form == POLAR_LEVEL_GAUSS && hp.key_floor == POLAR_KEY_FLOOR_NULL &&
+         hp.sat_form == POLAR_SAT_LOG && hp.window == 0;
+}
+
 // Per-head tables -> kernel constants.  Checks the values the maths needs: finite
-// parameters, kappa > 0, and a positive length temperature over the visible counts
-// 1..seq_k (lam is affine in ln n, so checking n = seq_k suffices).
+// parameters, kappa > 0, and a non-negative length temperature over the visible counts
+// 1..seq_k, positive from n = 2 on (lam is affine in ln n, so checking n = seq_k suffices
+// for 1 + tau ln n; tau ln n needs tau >= 0).
 polar_status head_params(const polar_problem* pr, HeadParams& hp, int& stride, int& floor_on, float& scale) {
+  const polar_status vst = variant_params(pr, hp);
+  if (vst != POLAR_OK) return vst;
   const bool any = pr->len_temp || pr->null_bias || pr->count_scale;
   if (any && pr->heads > POLAR_MAX_PARAM_HEADS) return POLAR_ERR_UNSUPPORTED;
   const int n = any ? pr->heads : 1;
@@ -97,7 +128,8 @@ polar_status head_params(const polar_problem* pr, HeadParams& hp, int& stride, i
     const float kappa = pr->count_scale ? pr->count_scale[h] : 1.0f;
     if (!std::isfinite(tau) || !std::isfinite(beta) || !std::isfinite(kappa) || !(kappa > 0.0f))
       return POLAR_ERR_BAD_PARAM;
-    if (!(1.0 + (double)tau * ln_tk > 0.0)) return POLAR_ERR_BAD_PARAM;
+    if (hp.lam_form == POLAR_TEMP_LOG && !(1.0 + (double)tau * ln_tk > 0.0)) return POLAR_ERR_BAD_PARAM;
+    if (hp.lam_form == POLAR_TEMP_SSMAX && !(tau >= 0.0f)) return POLAR_ERR_BAD_PARAM;
     hp.tau[h] = tau;
     hp.beta[h] = beta;
     hp.kinv[h] = 1.0f / kappa;
@@ -132,6 +164,54 @@ polar_status launch(Kernel kernel, dim3 grid, dim3 block, const Params& params, 
   return hipGetLastError() == hipSuccess ? POLAR_OK : POLAR_ERR_HIP;
 }
 
+// Which entry point is checking a problem's reading variant.
+enum class Entry { kFwd, kPartial, kDecode, kMerge, kBwd };
+
+// Variant checks that depend on the entry point (after head_params has validated the
+// variant itself).  `have_q`: the merge can read the queries (decode), which the
+// data-adaptive floor level needs.
+polar_status check_entry_variant(const polar_problem* pr, const HeadParams& hp, Entry e, bool have_q) {
+  switch (e) {
+    case Entry::kBwd:
+      return default_variant(hp) ? POLAR_OK : POLAR_ERR_UNSUPPORTED;
+    case Entry::kFwd:
+      return hp.window > 0 && !pr->causal ? POLAR_ERR_UNSUPPORTED : POLAR_OK;
+    case Entry::kPartial:
+      return hp.window > 0 || hp.level_form == POLAR_LEVEL_QNORM ? POLAR_ERR_UNSUPPORTED : POLAR_OK;
+    case Entry::kMerge:
+      return hp.level_form == POLAR_LEVEL_QNORM && !have_q ? POLAR_ERR_UNSUPPORTED : POLAR_OK;
+    default:
+      return POLAR_OK;
+  }
+}
+
+// bf16 prefill with the key-floor and window flags of the variant.
+template <int D, bool CAUSAL, bool STATS, int KF>
+polar_status launch_bf16_kf(const FwdParams& fp, unsigned blocks, void* stream) {
+  constexpr int NB = D == 64 ? kBf16Nb_d64 : kBf16Nb_d128;
+  constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
+  constexpr int BN = D == 64 ? kBf16Bn_d64 : kBf16Bn_d128;
+  if constexpr (CAUSAL) {
+    if (fp.hp.window > 0)
+      return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, true>, dim3(blocks),
+                    dim3(kBf16Waves * 64), fp, stream);
+  }
+  return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, false>, dim3(blocks),
+                dim3(kBf16Waves * 64), fp, stream);
+}
+
+template <int D, bool CAUSAL, bool STATS>
+polar_status launch_bf16(const FwdParams& fp, unsigned blocks, void* stream) {
+  switch (fp.hp.key_floor) {
+    case POLAR_KEY_FLOOR_SOFT:
+      return launch_bf16_kf<D, CAUSAL, STATS, POLAR_KEY_FLOOR_SOFT>(fp, blocks, stream);
+    case POLAR_KEY_FLOOR_GATE:
+      return launch_bf16_kf<D, CAUSAL, STATS, POLAR_KEY_FLOOR_GATE>(fp, blocks, stream);
+    default:
+      return launch_bf16_kf<D, CAUSAL, STATS, POLAR_KEY_FLOOR_NULL>(fp, blocks, stream);
+  }
+}
+
 template <int D, bool CAUSAL>
 polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
   const long long BH = (long long)pr->batch * pr->heads;
@@ -141,14 +221,9 @@ polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
     fp.n_qt = (pr->seq_q + BM - 1) / BM;
     const long long blocks = (long long)fp.n_qt * BH;
     if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-    constexpr int OCC = D == 64 ? kBf16Occ_d64 : kBf16Occ_d128;
-    constexpr int BN = D == 64 ? kBf16Bn_d64 : kBf16Bn_d128;
-    // the variant without statistics does not track the true row maximum
-    if (fp.stats || fp.part)
-      return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, true>, dim3((unsigned)blocks),
-                    dim3(kBf16Waves * 64), fp, stream);
-    return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, false>, dim3((unsigned)blocks),
-                  dim3(kBf16Waves * 64), fp, stream);
+    // the instantiation without statistics does not track the true row maximum
+    if (fp.stats || fp.part) return launch_bf16<D, CAUSAL, true>(fp, (unsigned)blocks, stream);
+    return launch_bf16<D, CAUSAL, false>(fp, (unsigned)blocks, stream);
   }
   fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;
   const long long blocks = (long long)fp.n_qt * BH;
@@ -209,18 +284,46 @@ polar_status check_paged(const polar_problem* pr, const polar_paged_kv* kv, int3
   return POLAR_OK;
 }
 
-template <int D, bool PAGED>
-polar_status launch_group(int chunk, polar::GroupDecodeParams& gp, dim3 grid, void* stream) {
+template <int D, bool PAGED, int KF>
+polar_status launch_group_kf(int chunk, polar::GroupDecodeParams& gp, dim3 grid, void* stream) {
   constexpr int NW = kDecodeWaves;
   switch (chunk) {
     case 1:
-      return launch(polar::polar_decode_group_kernel<D, 1, NW, 8, PAGED>, grid, dim3(NW * 64), gp, stream);
+      return launch(polar::polar_decode_group_kernel<D, 1, NW, 8, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
     case 2:
-      return launch(polar::polar_decode_group_kernel<D, 2, NW, 4, PAGED>, grid, dim3(NW * 64), gp, stream);
+      return launch(polar::polar_decode_group_kernel<D, 2, NW, 4, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
     case 4:
-      return launch(polar::polar_decode_group_kernel<D, 4, NW, 2, PAGED>, grid, dim3(NW * 64), gp, stream);
+      return launch(polar::polar_decode_group_kernel<D, 4, NW, 2, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
     default:
-      return launch(polar::polar_decode_group_kernel<D, 8, NW, 2, PAGED>, grid, dim3(NW * 64), gp, stream);
+      return launch(polar::polar_decode_group_kernel<D, 8, NW, 2, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
+  }
+}
+
+template <int D, bool PAGED>
+polar_status launch_group(int chunk, polar::GroupDecodeParams& gp, dim3 grid, void* stream) {
+  switch (gp.hp.key_floor) {
+    case POLAR_KEY_FLOOR_SOFT:
+      return launch_group_kf<D, PAGED, POLAR_KEY_FLOOR_SOFT>(chunk, gp, grid, stream);
+    case POLAR_KEY_FLOOR_GATE:
+      return launch_group_kf<D, PAGED, POLAR_KEY_FLOOR_GATE>(chunk, gp, grid, stream);
+    default:
+      return launch_group_kf<D, PAGED, POLAR_KEY_FLOOR_NULL>(chunk, gp, grid, stream);
+  }
+}
+
+template <int D>
+polar_status launch_split(const DecodeParams& dp, dim3 grid, void* stream) {
+  const dim3 block(kDecodeWaves * 64);
+  switch (dp.hp.key_floor) {
+    case POLAR_KEY_FLOOR_SOFT:
+      return launch(polar::polar_decode_split_kernel<D, kDecodeWaves, kDecodeUnroll, POLAR_KEY_FLOOR_SOFT>, grid, block,
+                    dp, stream);
+    case POLAR_KEY_FLOOR_GATE:
+      return launch(polar::polar_decode_split_kernel<D, kDecodeWaves, kDecodeUnroll, POLAR_KEY_FLOOR_GATE>, grid, block,
+                    dp, stream);
+    default:
+      return launch(polar::polar_decode_split_kernel<D, kDecodeWaves, kDecodeUnroll, POLAR_KEY_FLOOR_NULL>, grid, block,
+                    dp, stream);
   }
 }
 
@@ -243,7 +346,9 @@ polar_status launch_grouped_splits(const polar_problem* pr, const polar_paged_kv
   gp.Hkv = pr->kv_heads;
   gp.Tk = pr->seq_k;
   gp.S = splits;
-  gp.split_len = (pr->seq_k + splits - 1) / splits;
+  // the splits cover the last min(window, seq_k) keys of the longest sequence
+  const int keys = gp.hp.window > 0 && gp.hp.window < pr->seq_k ? gp.hp.window : pr->seq_k;
+  gp.split_len = (keys + splits - 1) / splits;
   gp.chunks = (pr->heads / pr->kv_heads) / chunk;
   if (kv) {
     gp.table = kv->block_table;
@@ -270,15 +375,16 @@ polar_status launch_merge(const polar_problem* pr, MergeParams& mp, void* stream
 }
 
 polar_status merge_with_lens(const polar_problem* pr, const float* partials, int32_t num_splits,
-                             const int32_t* lens, const polar_outputs* out, void* stream) {
+                             const int32_t* lens, const void* q, const polar_outputs* out, void* stream) {
   bool empty = false;
   polar_status st = check_shape(pr, empty);
   if (st != POLAR_OK) return st;
   if (num_splits < 1) return POLAR_ERR_BAD_SHAPE;
   MergeParams mp;
   std::memset(&mp, 0, sizeof(mp));
-  float scale_unused = 0.0f;
-  st = head_params(pr, mp.hp, mp.hp_stride, mp.floor_on, scale_unused);
+  st = head_params(pr, mp.hp, mp.hp_stride, mp.floor_on, mp.scale);
+  if (st != POLAR_OK) return st;
+  st = check_entry_variant(pr, mp.hp, Entry::kMerge, q != nullptr);
   if (st != POLAR_OK) return st;
   if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
   if (!partials) return POLAR_ERR_NULL_ARG;
@@ -288,6 +394,7 @@ polar_status merge_with_lens(const polar_problem* pr, const float* partials, int
   st = check_outputs(pr, out, ins, in_bytes, 1);
   if (st != POLAR_OK) return st;
   mp.part = partials;
+  mp.q = static_cast<const __bf16*>(q);
   mp.lens = lens;
   mp.dir = out->direction;
   mp.neff = out->n_eff;
@@ -362,6 +469,8 @@ polar_status polar_attn_fwd(const polar_problem* pr, const void* q, const void* 
   std::memset(&fp, 0, sizeof(fp));
   st = head_params(pr, fp.hp, fp.hp_stride, fp.floor_on, fp.scale);
   if (st != POLAR_OK) return st;
+  st = check_entry_variant(pr, fp.hp, Entry::kFwd, true);
+  if (st != POLAR_OK) return st;
   if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
   if (!q || !k || !v) return POLAR_ERR_NULL_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return POLAR_ERR_MISALIGNED;
@@ -404,7 +513,7 @@ size_t polar_attn_decode_workspace_bytes(const polar_problem* pr, int32_t num_sp
 
 polar_status polar_attn_merge(const polar_problem* pr, const float* partials, int32_t num_splits,
                               const polar_outputs* out, void* stream) {
-  return merge_with_lens(pr, partials, num_splits, nullptr, out, stream);
+  return merge_with_lens(pr, partials, num_splits, nullptr, nullptr, out, stream);
 }
 
 
@@ -418,6 +527,8 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
   std::memset(&dp, 0, sizeof(dp));
   int floor_on = 0;
   st = head_params(pr, dp.hp, dp.hp_stride, floor_on, dp.scale);
+  if (st != POLAR_OK) return st;
+  st = check_entry_variant(pr, dp.hp, Entry::kDecode, true);
   if (st != POLAR_OK) return st;
   if (pr->batch == 0 || pr->seq_q == 0) return POLAR_OK;  // no rows: pointers may be NULL
   if (!q || !k_cache || !v_cache) return POLAR_ERR_NULL_ARG;
@@ -444,18 +555,19 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
   dp.Hkv = pr->kv_heads;
   dp.Tk = pr->seq_k;
   dp.S = splits;
-  dp.split_len = (pr->seq_k + splits - 1) / splits;
+  // the query sees the last min(window, seq_k) keys
+  const int keys = dp.hp.window > 0 && dp.hp.window < pr->seq_k ? dp.hp.window : pr->seq_k;
+  dp.key0 = pr->seq_k - keys;
+  dp.split_len = (keys + splits - 1) / splits;
   const dim3 grid(splits, pr->heads, pr->batch);
   if (pr->heads > pr->kv_heads)  // grouped: every KV row is read once per group chunk
     st = launch_grouped_splits(pr, nullptr, q, k_cache, v_cache, splits, workspace, stream);
   else if (pr->head_dim == 64)
-    st = launch(polar::polar_decode_split_kernel<64, kDecodeWaves, kDecodeUnroll>, grid, dim3(kDecodeWaves * 64),
-                dp, stream);
+    st = launch_split<64>(dp, grid, stream);
   else
-    st = launch(polar::polar_decode_split_kernel<128, kDecodeWaves, kDecodeUnroll>, grid, dim3(kDecodeWaves * 64),
-                dp, stream);
+    st = launch_split<128>(dp, grid, stream);
   if (st != POLAR_OK) return st;
-  return polar_attn_merge(pr, (const float*)workspace, splits, out, stream);
+  return merge_with_lens(pr, (const float*)workspace, splits, nullptr, q, out, stream);
 }
 
 int32_t polar_attn_decode_paged_num_splits(const polar_problem* pr, const polar_paged_kv* kv, int32_t num_splits) {
@@ -484,6 +596,8 @@ polar_status polar_attn_decode_paged(const polar_problem* pr, const void* q, con
     float scale = 0.0f;
     st = head_params(pr, hp, stride, floor_on, scale);
     if (st != POLAR_OK) return st;
+    st = check_entry_variant(pr, hp, Entry::kDecode, true);
+    if (st != POLAR_OK) return st;
   }
   if (pr->batch == 0 || pr->seq_q == 0) return POLAR_OK;  // no rows: pointers may be NULL
   if (!q || !kv->k_pool || !kv->v_pool || !kv->block_table || !kv->seq_lens) return POLAR_ERR_NULL_ARG;
@@ -507,7 +621,7 @@ polar_status polar_attn_decode_paged(const polar_problem* pr, const void* q, con
   if (st != POLAR_OK) return st;
   polar_problem flat = *pr;
   flat.causal = 0;
-  return merge_with_lens(&flat, (const float*)workspace, splits, kv->seq_lens, out, stream);
+  return merge_with_lens(&flat, (const float*)workspace, splits, kv->seq_lens, q, out, stream);
 }
 
 polar_status polar_attn_fwd_partial(const polar_problem* pr, const void* q, const void* k, const void* v,
@@ -520,11 +634,13 @@ polar_status polar_attn_fwd_partial(const polar_problem* pr, const void* q, cons
   std::memset(&fp, 0, sizeof(fp));
   st = head_params(pr, fp.hp, fp.hp_stride, fp.floor_on, fp.scale);
   if (st != POLAR_OK) return st;
+  st = check_entry_variant(pr, fp.hp, Entry::kPartial, true);
+  if (st != POLAR_OK) return st;
   if (num_splits < 1 || split < 0 || split >= num_splits) return POLAR_ERR_BAD_SHAPE;
   if (context_k != 0) {
     if (context_k < pr->seq_q || context_k < 0) return POLAR_ERR_BAD_SHAPE;
     // the temperature must stay positive at the longest context count
-    const int nh = pr->len_temp ? pr->heads : 0;
+    const int nh = pr->len_temp && fp.hp.lam_form == POLAR_TEMP_LOG ? pr->heads : 0;
     for (int h = 0; h < nh; ++h)
       if (!(1.0 + (double)pr->len_temp[h] * std::log((double)context_k) > 0.0)) return POLAR_ERR_BAD_PARAM;
   }
@@ -570,6 +686,8 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   polar::BwdParams bp;
   std::memset(&bp, 0, sizeof(bp));
   st = head_params(pr, bp.hp, bp.hp_stride, bp.floor_on, bp.scale);
+  if (st != POLAR_OK) return st;
+  st = check_entry_variant(pr, bp.hp, Entry::kBwd, true);
   if (st != POLAR_OK) return st;
   if (!g) return POLAR_ERR_NULL_ARG;
   if (pr->batch == 0) return POLAR_OK;  // nothing to write

@@ -32,11 +32,18 @@ constexpr float kRescaleSlack = 8.0f;
 // weights of one tile sum to more than 2^8 (every weight is then at most 2^8).
 constexpr float kWeightLimit = 256.0f;
 
-// Per-head parameters, copied by value into the kernel arguments.
+// Per-head parameters and the reading variant, copied by value into the kernel
+// arguments.
 struct HeadParams {
   float tau[POLAR_MAX_PARAM_HEADS];   // length temperature
   float beta[POLAR_MAX_PARAM_HEADS];  // null-floor offset
   float kinv[POLAR_MAX_PARAM_HEADS];  // 1 / kappa
+  int lam_form;                       // polar_temperature_form
+  float inv_ln_train;                 // 1 / ln L for POLAR_TEMP_TRAIN_RATIO
+  int level_form;                     // polar_floor_level
+  int key_floor;                      // polar_key_floor
+  int sat_form;                       // polar_saturation
+  int window;                         // > 0: keys per sliding window
 };
 
 struct FwdParams {
@@ -66,6 +73,7 @@ struct DecodeParams {
   const void* v;
   float* part;    // [B, H, S, D + 3]
   int B, H, Hkv, Tk;
+  int key0;       // first key of split 0 (the start of a sliding window)
   int S;          // splits
   int split_len;  // keys per split (the last one may be shorter)
   float scale;
@@ -75,6 +83,8 @@ struct DecodeParams {
 
 struct MergeParams {
   const float* part;  // [B, H, Tq, S, D + 3]
+  const __bf16* q;    // [B, H, Tq, D] for the data-adaptive floor level, else unused
+  float scale;
   const int32_t* lens;  // optional [B]: visible count of sequence b (one query per sequence)
   float* dir;
   float* neff;
@@ -104,27 +114,61 @@ __device__ __forceinline__ int context_count(int row, int Tq, int Tk, bool causa
   return visible_keys(row, Tq, Tk, causal);
 }
 
-// Length temperature lam(n) = 1 + tau ln n [ATMA §2.1, direction channel].
-__device__ __forceinline__ float length_temperature(float tau, int n) {
-  return 1.0f + tau * logf((float)n);
+// Length temperature [ATMA §2.1, direction channel], by the form of the variant:
+// 1 + tau ln n (the default), tau ln n, or ln n / ln L.
+__device__ __forceinline__ float row_temperature(const HeadParams& hp, int hpi, int n) {
+  const float ln_n = logf((float)n);
+  if (hp.lam_form == POLAR_TEMP_SSMAX) return hp.tau[hpi] * ln_n;
+  if (hp.lam_form == POLAR_TEMP_TRAIN_RATIO) return ln_n * hp.inv_ln_train;
+  return 1.0f + hp.tau[hpi] * ln_n;
+}
+
+// Base-2 logit scale c = lam * scale * log2(e).  lam may be 0 (tau ln n at n = 1); c is
+// then held at a tiny positive value, so masked scores stay -inf (never 0 * -inf) while
+// every visible exp2(c s - m) is exactly what c = 0 gives in fp32.
+__device__ __forceinline__ float logit_scale(float lam, float scale) {
+  return fmaxf(lam * scale * kLog2e, 1.0e-30f);
+}
+
+// Expected maximum of n standard normal logits [ATMA §2.1, extreme-value-corrected
+// floor]: sqrt(2 ln n) to leading order, or the second-order Gumbel mean
+// b_n + gamma a_n with r = sqrt(2 ln n), b_n = r - (ln ln n + ln 4 pi) / (2 r), a_n = 1 / r.
+// One logit has mean 0.
+__device__ __forceinline__ float floor_level(const HeadParams& hp, int n) {
+  if (n <= 1) return 0.0f;
+  const float ln_n = logf((float)n);
+  const float r = sqrtf(2.0f * ln_n);
+  if (hp.level_form == POLAR_LEVEL_GUMBEL2) {
+    constexpr float kLn4Pi = 2.5310242469692907f;
+    constexpr float kEulerGamma = 0.5772156649015329f;
+    return r - (logf(ln_n) + kLn4Pi) / (2.0f * r) + kEulerGamma / r;
+  }
+  return r;
+}
+
+// Null floor f = lam sigma l(n) + beta in tempered-logit units; sigma is 1, or
+// scale ||q|| for the data-adaptive level (the spread of the raw logits of the row).
+__device__ __forceinline__ float null_floor(const HeadParams& hp, int hpi, int n, float lam, float sigma) {
+  return lam * sigma * floor_level(hp, n) + hp.beta[hpi];
 }
 
 // Magnitude channel from the row statistics [ATMA §2.1]:
 //   n_eff = S1^2 / S2 (participation ratio),
-//   conf  = S1 / (S1 + exp(f - m)) with the null floor f = lam sqrt(2 ln n) + beta,
-//   count = conf * tanh(ln(n_eff) / kappa).
+//   conf  = S1 / (S1 + exp(f - m)) with the null floor f (1 when the floor is off),
+//   count = conf * tanh(ln(n_eff) / kappa), or tanh(ln(1 + n_eff) / kappa).
 // m_nat is the row maximum in natural-log units; S1, S2 are relative to exp(m_nat).
-__device__ __forceinline__ void magnitude_channel(float m_nat, float S1, float S2, int n, float lam,
-                                                  bool floor_on, float beta, float kinv,
-                                                  float& neff, float& conf, float& count) {
-  neff = S1 * S1 / S2;
-  if (floor_on) {
-    const float f = lam * sqrtf(2.0f * logf((float)n)) + beta;
-    conf = 1.0f / (1.0f + expf(f - m_nat - logf(S1)));
-  } else {
-    conf = 1.0f;
+// With a per-key floor S1 may be 0 (no key above the floor): every channel is then 0.
+__device__ __forceinline__ void magnitude_channel(const HeadParams& hp, int hpi, float m_nat, float S1, float S2,
+                                                  float f, bool floor_on, float& neff, float& conf,
+                                                  float& count) {
+  if (!(S1 > 0.0f)) {
+    neff = conf = count = 0.0f;
+    return;
   }
-  count = conf * tanhf(logf(neff) * kinv);
+  neff = S1 * S1 / S2;
+  conf = floor_on ? 1.0f / (1.0f + expf(f - m_nat - logf(S1))) : 1.0f;
+  const float x = hp.sat_form == POLAR_SAT_LOG1P ? log1pf(neff) : logf(neff);
+  count = conf * tanhf(x * hp.kinv[hpi]);
 }
 
 // Block id -> (query tile, b*H + h).  Consecutive block ids are dispatched round-robin

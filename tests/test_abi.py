@@ -66,7 +66,9 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
         "F(polar_problem, batch) F(polar_problem, heads) F(polar_problem, kv_heads) F(polar_problem, seq_q)\n"
         "F(polar_problem, seq_k) F(polar_problem, head_dim) F(polar_problem, causal) F(polar_problem, dtype)\n"
         "F(polar_problem, softmax_scale) F(polar_problem, len_temp) F(polar_problem, null_bias)\n"
-        "F(polar_problem, count_scale)\n"
+        "F(polar_problem, count_scale) F(polar_problem, variant)\n"
+        "F(polar_variant, temperature) F(polar_variant, train_len) F(polar_variant, floor_level)\n"
+        "F(polar_variant, key_floor) F(polar_variant, saturation) F(polar_variant, window)\n"
         "F(polar_outputs, direction) F(polar_outputs, n_eff) F(polar_outputs, confidence) F(polar_outputs, count)\n"
         "F(polar_outputs, stats)\n"
         "F(polar_paged_kv, k_pool) F(polar_paged_kv, v_pool) F(polar_paged_kv, block_table)\n"
@@ -76,12 +78,13 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
         'printf("sizeof polar_problem %zu\\nsizeof polar_outputs %zu\\n", sizeof(polar_problem), sizeof(polar_outputs));\n'
         'printf("sizeof polar_paged_kv %zu\\n", sizeof(polar_paged_kv));\n'
         'printf("sizeof polar_grads %zu\\n", sizeof(polar_grads));\n'
+        'printf("sizeof polar_variant %zu\\n", sizeof(polar_variant));\n'
         "return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
     classes = {"polar_problem": pa.PolarProblem, "polar_outputs": pa.PolarOutputs, "polar_paged_kv": pa.PolarPagedKV,
-               "polar_grads": pa.PolarGrads}
+               "polar_grads": pa.PolarGrads, "polar_variant": pa.PolarVariant}
     for line in filter(None, lines):
         a, b, c = line.split()
         if a == "sizeof":
@@ -335,6 +338,60 @@ def test_bwd_validation(lib):
     # the (batch, head) grid dimension is limited to 65535 pairs
     big, keep6 = good_problem(batch=40000, heads=2, kv_heads=2).to_c()
     assert run(problem=big) == 3
+
+
+@pytest.mark.parametrize("variant,status", [
+    (dict(temperature="log"), 0), (dict(window=-1), 4), (dict(temperature="train_ratio", train_len=1), 4),
+    (dict(key_floor="soft"), 4),                      # a per-key floor without the floor
+    (dict(window=16), 0),
+])
+def test_fwd_variant_validation(lib, variant, status):
+    """Variant checks run before any launch; the calls that pass them fail on the fake
+    output pointer overlap check instead (status 7), so nothing is launched."""
+    prob = good_problem(variant=variant)
+    out = outputs(direction=fake(2))  # overlaps k: the call stops at the alias check
+    got = call_fwd(lib, prob, out=out)
+    assert got == (7 if status == 0 else status)
+
+
+def test_variant_enum_and_entry_checks(lib):
+    def problem(**v):
+        pr, keep = good_problem(null_bias=[0.0, 0.0]).to_c()
+        var = pa.PolarVariant(v.get("t", 0), v.get("L", 2048), v.get("fl", 0), v.get("kf", 0), v.get("sat", 0),
+                              v.get("w", 0))
+        pr.variant = ctypes.pointer(var)
+        return pr, (keep, var)
+
+    def fwd(pr):
+        o = outputs(direction=fake(2))
+        return lib.polar_attn_fwd(ctypes.byref(pr), fake(1), fake(2), fake(3), ctypes.byref(o), None)
+
+    for bad in (dict(t=3), dict(t=-1), dict(fl=3), dict(kf=3), dict(sat=2)):
+        pr, keep = problem(**bad)
+        assert fwd(pr) == 3, bad
+    # ssmax needs tau >= 0
+    pr, keep = problem(t=1)
+    neg = (ctypes.c_float * 2)(0.5, -0.1)
+    pr.len_temp = ctypes.cast(neg, ctypes.POINTER(ctypes.c_float))
+    assert fwd(pr) == 4
+    # a window needs the causal alignment in prefill
+    pr, keep = problem(w=8)
+    pr.causal = 0
+    assert fwd(pr) == 3
+    # the partial forward takes neither a window nor the data-adaptive level
+    for v in (dict(w=8), dict(fl=2)):
+        pr, keep = problem(**v)
+        assert lib.polar_attn_fwd_partial(ctypes.byref(pr), fake(1), fake(2), fake(3), 0, fake(4), 2, 0, None) == 3
+    # the public merge has no queries for the data-adaptive level
+    pr, keep = problem(fl=2)
+    o = outputs()
+    assert lib.polar_attn_merge(ctypes.byref(pr), fake(4), 2, ctypes.byref(o), None) == 3
+    # the backward computes the default reading only
+    for v in (dict(kf=1), dict(w=4), dict(sat=1), dict(t=2), dict(fl=1)):
+        pr, keep = problem(**v)
+        g = pa.PolarGrads(None, None, None, None)
+        assert lib.polar_attn_bwd(ctypes.byref(pr), fake(1), fake(2), fake(3), ctypes.byref(g), fake(4), fake(5),
+                                  fake(6), fake(7), 1 << 30, None) == 3, v
 
 
 def test_python_binding_checks():
