@@ -43,12 +43,39 @@ PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 2.4 GHz x 256 flop/
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
-def source_digest():
-    h = hashlib.sha256()
+# Sources each profiled kernel is built from (besides the shared header, the ABI header
+# and the launch-geometry constants of the host file).
+KERNEL_SOURCES = {
+    "fwd_bf16_t65536_d64": ["fwd_bf16.h"],
+    "fwd_bf16_t16384_d128": ["fwd_bf16.h"],
+    "decode_b64_h8_tk65536_d128": ["decode.h"],
+    "merge_b64_h8_d128": ["decode.h"],
+    "paged_gqa_decode_b64_h32_kv8_tk65536_d128": ["decode_group.h", "decode.h"],
+    "bwd_rows_b1_h16_kv4_t16384_d128": ["bwd.h"],
+    "bwd_dq_b1_h16_kv4_t16384_d128": ["bwd.h"],
+    "bwd_dkdv_b1_h16_kv4_t16384_d128": ["bwd.h"],
+}
+
+
+def source_digest(kernel_key=None):
+    """Digest of the sources a kernel is built from: its headers, polar_common.h, the ABI
+    header and the launch-geometry lines of polar_attn.hip (all of csrc/ when no kernel
+    is named).  A profile stays valid while this digest is unchanged."""
     csrc = os.path.join(ROOT, "long_context_attention_polar_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    h = hashlib.sha256()
+    if kernel_key is None:
+        names = sorted(os.listdir(csrc))
+    else:
+        names = sorted(set(KERNEL_SOURCES[kernel_key]) | {"polar_common.h"})
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    if kernel_key is not None:
+        with open(os.path.join(ROOT, "include", "polar_attn.h"), "rb") as f:
+            h.update(f.read())
+        with open(os.path.join(csrc, "polar_attn.hip")) as f:
+            geometry = [ln for ln in f if ln.lstrip().startswith(("constexpr int k", "#define POLAR_"))]
+        h.update("".join(geometry).encode())
     return h.hexdigest()[:16]
 
 
@@ -70,14 +97,16 @@ def decode_bytes(w):
     return kv + q + outs
 
 
-def measured_traffic(kernel_key, digest):
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed PMC digest, or None when the kernel's
+    sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     entry = data.get(kernel_key)
-    if not entry or entry.get("source_digest") != digest:
+    if not entry or entry.get("source_digest") != source_digest(kernel_key):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -255,11 +284,11 @@ def main():
     big = res[PREFILL[1]]
     roofline = {"bound": "mfma", "achieved": big["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": big["tflops"] / PEAK_BF16_TFLOPS, "kernel": "polar_fwd_bf16_kernel<64,...> (T=65536 d=64)",
-                "traffic": measured_traffic("fwd_bf16_t65536_d64", digest)}
+                "traffic": measured_traffic("fwd_bf16_t65536_d64")}
     dec = res[DECODE]
     decode_roof = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": dec["frac_hbm_peak"], "ms": dec["ms_avg"],
-                   "traffic": measured_traffic("decode_b64_h8_tk65536_d128", digest)}
+                   "traffic": measured_traffic("decode_b64_h8_tk65536_d128")}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
@@ -272,9 +301,11 @@ def main():
         "decode": decode_roof,
         "paged_gqa_decode": {"bound": "hbm", "achieved": res[PAGED]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": res[PAGED]["frac_hbm_peak"], "ms": res[PAGED]["ms_avg"],
+                             "traffic": measured_traffic("paged_gqa_decode_b64_h32_kv8_tk65536_d128"),
                              "note": "32 query heads share 8 KV heads; K and V are read once per group"},
         "backward": {"bound": "alu", "achieved": res[BWD]["tflops"], "peak": PEAK_F32_VALU_TFLOPS,
                      "unit": "TFLOP/s", "frac": res[BWD]["frac_f32_valu_peak"], "ms": res[BWD]["ms_avg"],
+                     "traffic_dkdv": measured_traffic("bwd_dkdv_b1_h16_kv4_t16384_d128"),
                      "note": "three fp32 vector-ALU kernels; 10 d algorithmic flops per causal pair"},
         "parts": res,
         "source_digest": digest,
