@@ -11,9 +11,9 @@ already resident in HBM:
   * grouped split-KV decode + merge over a paged cache, bf16, batch 64, 32 query heads
     over 8 KV heads, d=128, 65536 keys per sequence in shuffled 16-row blocks (reported
     beside the headline, not part of it);
-  * backward (dq, dk, dv for upstream gradients of all four channels), bf16 inputs,
-    B=1, 16 query heads over 4 KV heads, T=16384, d=128, causal (reported beside the
-    headline, not part of it, and timed in a loop of its own after the steps).
+  * backward (dq, dk, dv for upstream gradients of all four channels), bf16 inputs on the
+    matrix cores, B=1, 16 query heads over 4 KV heads, T=16384, d=128, causal (reported
+    beside the headline, not part of it, and timed in a loop of its own after the steps).
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -39,7 +39,6 @@ PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
 DECODE = "bf16_decode_b64_h8_tk65536_d128"
 PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
 BWD = "bf16_bwd_b1_h16_kv4_t16384_d128"
-PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 2.4 GHz x 256 flop/clk
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -51,9 +50,9 @@ KERNEL_SOURCES = {
     "decode_b64_h8_tk65536_d128": ["decode.h"],
     "merge_b64_h8_d128": ["decode.h"],
     "paged_gqa_decode_b64_h32_kv8_tk65536_d128": ["decode_group.h", "decode.h"],
-    "bwd_rows_b1_h16_kv4_t16384_d128": ["bwd.h"],
-    "bwd_dq_b1_h16_kv4_t16384_d128": ["bwd.h"],
-    "bwd_dkdv_b1_h16_kv4_t16384_d128": ["bwd.h"],
+    "bwd_dq_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
+    "bwd_dk_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
+    "bwd_dv_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
 }
 
 
@@ -267,7 +266,7 @@ def main():
             entry["flops_per_launch"] = p["flops"]
         elif p["kind"] == "backward":
             entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
-            entry["frac_f32_valu_peak"] = entry["tflops"] / PEAK_F32_VALU_TFLOPS
+            entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
             entry["flops_per_call"] = p["flops"]
         else:
             entry["gbs"] = p["bytes"] / (avg * 1e-3) / 1e9
@@ -303,10 +302,11 @@ def main():
                              "frac": res[PAGED]["frac_hbm_peak"], "ms": res[PAGED]["ms_avg"],
                              "traffic": measured_traffic("paged_gqa_decode_b64_h32_kv8_tk65536_d128"),
                              "note": "32 query heads share 8 KV heads; K and V are read once per group"},
-        "backward": {"bound": "alu", "achieved": res[BWD]["tflops"], "peak": PEAK_F32_VALU_TFLOPS,
-                     "unit": "TFLOP/s", "frac": res[BWD]["frac_f32_valu_peak"], "ms": res[BWD]["ms_avg"],
-                     "traffic_dkdv": measured_traffic("bwd_dkdv_b1_h16_kv4_t16384_d128"),
-                     "note": "three fp32 vector-ALU kernels; 10 d algorithmic flops per causal pair"},
+        "backward": {"bound": "mfma", "achieved": res[BWD]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": res[BWD]["frac_bf16_peak"], "ms": res[BWD]["ms_avg"],
+                     "traffic_dk": measured_traffic("bwd_dk_b1_h16_kv4_t16384_d128"),
+                     "note": "bf16 matrix-core path: forward statistics, row constants, dq, dk, dv; "
+                             "10 d algorithmic flops per causal pair"},
         "parts": res,
         "source_digest": digest,
     }

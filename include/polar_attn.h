@@ -277,8 +277,10 @@ typedef struct polar_grads {
   const float* d_count;
 } polar_grads;
 
-/* Bytes of device workspace polar_attn_bwd needs: B * heads * seq_q * (head_dim + 4)
- * fp32 (per query row, the vector w and four row constants).  0 when the problem is
+/* Bytes of device workspace polar_attn_bwd needs.  fp32 inputs: B * heads * seq_q *
+ * (head_dim + 4) fp32 (per query row, the vector w and four row constants).  bf16 inputs:
+ * per query row the forward's statistics (head_dim + 3 fp32), w (head_dim bf16) and four
+ * row constants (fp32), in three parts each padded to 256 bytes.  0 when the problem is
  * invalid (or has no query rows). */
 size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
 
@@ -298,14 +300,16 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
  *   ds_ij = p_ij (c1 + 2 c2 p_ij + <w, v_j>),
  *   dq_i = lam_i scale sum_j ds_ij k_j,  dk_j = sum_i lam_i scale ds_ij q_i,  dv_j = sum_i p_ij w_i,
  * dk and dv summed over the query heads that share a KV head.  Same problem rules as
- * polar_attn_fwd (bf16 or fp32 inputs, head_dim 64 or 128, causal or not); fp32
- * arithmetic; batch * heads <= 65535.  Outputs are DEVICE fp32, 16-byte aligned and
+ * polar_attn_fwd (bf16 or fp32 inputs, head_dim 64 or 128, causal or not).  fp32 inputs
+ * run in fp32 on the vector ALUs (batch * heads <= 65535).  bf16 inputs run on the
+ * matrix cores: the row statistics come from the forward kernel (bf16 weights), and
+ * P, dS and w enter the products as bf16 with fp32 sums.  Outputs are DEVICE fp32, 16-byte aligned and
  * overwritten: dq [B, heads, seq_q, head_dim], dk and dv [B, kv_heads, seq_k, head_dim].
  * `workspace` (DEVICE, 16-byte aligned, polar_attn_bwd_workspace_bytes bytes) is
  * scratch owned by the call until the stream reaches its end.  No output or the
  * workspace may overlap an input or another output.  batch == 0 enqueues nothing;
- * seq_q == 0 (q, dq and workspace may then be NULL) writes zero dk and dv.  Three
- * kernels run in order on `stream`. */
+ * seq_q == 0 (q, dq and workspace may then be NULL) writes zero dk and dv.  The kernels
+ * (three for fp32, four for bf16) run in order on `stream`. */
 polar_status polar_attn_bwd(const polar_problem* problem, const void* q, const void* k, const void* v,
                             const polar_grads* grads, float* dq, float* dk, float* dv, void* workspace,
                             size_t workspace_bytes, void* stream);

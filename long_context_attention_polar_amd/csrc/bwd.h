@@ -53,6 +53,26 @@ struct BwdParams {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 32;  // rows per LDS tile
 
+// c1 and c2 of a row from its statistics (S1, S2 relative to e^{m_nat}) and upstream
+// gradients g_n, g_c, g_k of n_eff, the confidence and the count.
+__device__ __forceinline__ void row_constants(const HeadParams& hp, int hpi, bool floor_on, int n, float lam,
+                                              float m_nat, float s1, float s2, float g_n, float g_c, float g_k,
+                                              float& c1, float& c2) {
+  const float kinv = hp.kinv[hpi];
+  const float n_eff = s1 * s1 / s2;
+  float conf = 1.0f, dconf = 0.0f;
+  if (floor_on) {
+    const float f = null_floor(hp, hpi, n, lam, 1.0f);
+    conf = 1.0f / (1.0f + expf(f - m_nat - logf(s1)));
+    dconf = conf * (1.0f - conf);
+  }
+  const float t = tanhf(logf(n_eff) * kinv);
+  const float g_conf = g_c + g_k * t;
+  const float g_neff = g_n + g_k * conf * (1.0f - t * t) * kinv / n_eff;
+  c1 = (2.0f * g_neff * n_eff + g_conf * dconf) / s1;
+  c2 = -g_neff * n_eff / s2;
+}
+
 // Sum over the LPR (1, 2 or 4) neighbouring lanes of one row.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
@@ -203,19 +223,9 @@ __global__ __launch_bounds__(kBwdThreads) void polar_bwd_rows_kernel(const BwdPa
     const float g_n = p.g_neff ? p.g_neff[ri] : 0.0f;
     const float g_c = p.g_conf ? p.g_conf[ri] : 0.0f;
     const float g_k = p.g_count ? p.g_count[ri] : 0.0f;
-    const float kinv = p.hp.kinv[hpi];
-    const float n_eff = s1 * s1 / s2;
-    float conf = 1.0f, dconf = 0.0f;
-    if (p.floor_on) {
-      const float f = null_floor(p.hp, hpi, n, lam, 1.0f);
-      conf = 1.0f / (1.0f + expf(f - m * kLn2 - logf(s1)));
-      dconf = conf * (1.0f - conf);
-    }
-    const float t = tanhf(logf(n_eff) * kinv);
-    const float g_conf = g_c + g_k * t;
-    const float g_neff = g_n + g_k * conf * (1.0f - t * t) * kinv / n_eff;
-    const f32x4 rv = {m, (2.0f * g_neff * n_eff + g_conf * dconf) / s1, -g_neff * n_eff / s2, c};
-    *(f32x4*)(p.R + ri * 4) = rv;
+    float c1, c2;
+    row_constants(p.hp, hpi, p.floor_on != 0, n, lam, m * kLn2, s1, s2, g_n, g_c, g_k, c1, c2);
+    *(f32x4*)(p.R + ri * 4) = f32x4{m, c1, c2, c};
   }
 }
 

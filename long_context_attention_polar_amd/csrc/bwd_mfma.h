@@ -1,0 +1,467 @@
+// Backward pass on the matrix cores for bf16 inputs.
+//
+// The gradient is the one written out in bwd.h (chain rule through the forward
+// definition [ATMA §2.1]); its products have the shape of five matrix products per
+// (query tile, key tile), which run here as v_mfma_f32_32x32x16_bf16 with the operand
+// layouts of the bf16 forward kernel:
+//   rows   the forward kernel in partial mode gives every row's (m, S1, S2, acc); a small
+//          kernel turns them and the upstream gradients into w (bf16) and the row
+//          constants (m in base 2, c1, c2, c);
+//   dq     per query tile: S^T = K Q^T and G^T = V W^T (K, V rows from LDS, Q and W in
+//          registers, lane = query); dS = P (c1 + 2 c2 P + G) on the vector ALUs, rounded
+//          to bf16 in the B-operand key order; dQ^T += K^T dS^T with K^T read from the
+//          row-major K tile by transpose reads;
+//   dk/dv  per key tile, over the query rows of every query head of its GQA group:
+//          S = Q K^T and G = W V^T (Q, W rows from LDS, K and V in registers, lane = key);
+//          P and dS with the per-row constants read from LDS; dK^T += Q^T dS and
+//          dV^T += W^T P with Q^T and W^T from transpose reads.  At d = 128 the four
+//          accumulators and the K, V fragments do not fit one wave's share of two waves per
+//          SIMD, so dk (S, G, dK) and dv (S, dV) run as two kernels that each keep two
+//          waves per SIMD; S is computed in both.
+// P, dS and w enter the products as bf16 (round to nearest even); every sum is fp32.
+#pragma once
+
+#include "bwd.h"
+#include "fwd_bf16.h"
+
+namespace polar {
+
+struct BwdMfmaParams {
+  const __bf16* q;       // [B, H, Tq, D]
+  const __bf16* k;       // [B, Hkv, Tk, D]
+  const __bf16* v;
+  const float* part;     // [B, H, Tq, D + 3]: the forward's (m, S1, S2, acc) of every row
+  const float* g_dir;    // upstream gradients (null = 0)
+  const float* g_neff;
+  const float* g_conf;
+  const float* g_count;
+  __bf16* W;             // [B, H, Tq, D]: w of every row, bf16
+  f32x4* R;              // [B, H, Tq]: (m in base 2, c1, c2, c = lam scale log2 e)
+  float* dq;             // [B, H, Tq, D]
+  float* dk;             // [B, Hkv, Tk, D]
+  float* dv;
+  int B, H, Hkv, Tq, Tk;
+  int n_qt;              // query tiles per (b, h) of the dq kernel
+  int n_kt;              // key tiles per (b, kv head) of the dk/dv kernel
+  int floor_on;
+  int hp_stride;
+  float scale;
+  HeadParams hp;
+};
+
+// One wave per query row: w = (g_u - u (u . g_u)) / ||acc|| as bf16, and the row constants.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void polar_bwd_prep_kernel(const BwdMfmaParams p) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * H + h) * Tq + i
+  const size_t rows = (size_t)p.B * p.H * p.Tq;
+  if (row >= rows) return;  // whole waves leave together
+  const int i = (int)(row % p.Tq);
+  const int h = (int)((row / p.Tq) % p.H);
+  const float* pr = p.part + row * (D + 3);
+  float acc[DPL], gu[DPL];
+  float nn = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    acc[e] = pr[3 + lane + 64 * e];
+    gu[e] = p.g_dir ? p.g_dir[row * D + lane + 64 * e] : 0.0f;
+    nn = fmaf(acc[e], acc[e], nn);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) nn += __shfl_xor(nn, sh, 64);
+  const float a = sqrtf(nn);
+  const float inv_a = a > 0.0f ? 1.0f / a : 0.0f;  // acc == 0: zero direction, w = 0
+  float ug = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) ug = fmaf(acc[e] * inv_a, gu[e], ug);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) ug += __shfl_xor(ug, sh, 64);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) p.W[row * D + lane + 64 * e] = (__bf16)((gu[e] - acc[e] * inv_a * ug) * inv_a);
+  if (lane == 0) {
+    const int hpi = h * p.hp_stride;
+    const int n = visible_keys(i, p.Tq, p.Tk, CAUSAL);
+    const float lam = row_temperature(p.hp, hpi, n);
+    const float m_nat = pr[0];
+    float c1, c2;
+    row_constants(p.hp, hpi, p.floor_on != 0, n, lam, m_nat, pr[1], pr[2], p.g_neff ? p.g_neff[row] : 0.0f,
+                  p.g_conf ? p.g_conf[row] : 0.0f, p.g_count ? p.g_count[row] : 0.0f, c1, c2);
+    p.R[row] = f32x4{m_nat * kLog2e, c1, c2, logit_scale(lam, p.scale)};
+  }
+}
+
+// dq: a workgroup of NW waves owns 32 * NW query rows of one (b, h); keys stream through
+// LDS in double-buffered tiles of BN rows exactly as in the forward kernel.
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void polar_bwd_dq_mfma_kernel(
+    const BwdMfmaParams p) {
+  constexpr int BM = NW * 32;
+  constexpr int MB = BN / 32;
+  constexpr int KS = D / 16;
+  constexpr int DM = D / 32;
+  constexpr int PS = BN / 16;
+
+  __shared__ __attribute__((aligned(1024))) __bf16 k_buf0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_buf1[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_buf0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_buf1[BN * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int qt, bh;
+  tile_coords(blockIdx.x, p.n_qt, p.B * p.H, qt, bh);
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int hk = h / (p.H / p.Hkv);
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int off = Tk - Tq;
+  const int q0 = qt * BM;
+  const int wq0 = q0 + wave * 32;
+
+  const size_t kv_head = (size_t)(b * p.Hkv + hk) * Tk * D;
+  const uint32_t head_bytes = (uint32_t)((size_t)Tk * D * 2);
+  const __amdgpu_buffer_rsrc_t kb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_head), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_head), (short)0, head_bytes, 0x00020000);
+  const uint32_t voff = tile_lane_offset<D, NW>(wave, lane);
+
+  const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int wave_kmax = CAUSAL ? min(wq0 + 31 + off, Tk - 1) : Tk - 1;
+  const int wave_kmin = CAUSAL ? min(wq0 + off, Tk - 1) : Tk - 1;
+
+  load_tile<D, BN, NW>(kb, 0, voff, k_buf0, wave);
+  load_tile<D, BN, NW>(vb, 0, voff, v_buf0, wave);
+
+  const int qrow = wq0 + col;
+  const bool live = qrow < Tq;
+  const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
+  const size_t ri = (size_t)bh * Tq + qrow;
+  // a row past the end gets weight 0 everywhere (m = +inf); its output is never written
+  const f32x4 rv = live ? p.R[ri] : f32x4{INFINITY, 0.0f, 0.0f, 1.0e-30f};
+  const float neg_m = -rv[0], c1 = rv[1], c2x2 = 2.0f * rv[2], c = rv[3];
+
+  // Q^T and W^T fragments: lane holds row qrow, dims ks * 16 + 8 * half + [0, 8)
+  bf16x8 qf[KS], wf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (live) {
+      qf[ks] = *(const bf16x8*)(p.q + ri * D + ks * 16 + 8 * half);
+      wf[ks] = *(const bf16x8*)(p.W + ri * D + ks * 16 + 8 * half);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = wf[ks][e] = (__bf16)0.0f;
+    }
+  }
+
+  // LDS offsets: row reads of K and V (A operands of S^T and G^T) and transpose reads of
+  // K (A operand of dQ^T), as in the forward kernel
+  const int k_x = half ^ chunk_swizzle<D>(col);
+  const uint32_t k_base = (uint32_t)(col * D * 2 + 16 * (k_x & 1));
+  const uint32_t k_xor = (uint32_t)(32 * (k_x >> 1));
+  const int gi = lane & 15;
+  const int g = lane >> 4;
+  int t_off[2][DM];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * half + (gi >> 2);
+    const int sw = chunk_swizzle<D>(row);
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+      const int lchunk = 4 * dm + 2 * (g & 1) + ((gi & 3) >> 1);
+      t_off[r][dm] = row * D + ((lchunk ^ sw) << 3) + 4 * (gi & 1);
+    }
+  }
+
+  f32x16 dq[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[dm][e] = 0.0f;
+
+  auto compute_tile = [&](const __bf16* kt, const __bf16* vt, int kv0) __attribute__((always_inline)) {
+    f32x16 s[MB], gg[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[mb][e] = gg[mb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t o = (k_base + ((32u * ks) ^ k_xor)) + mb * 32 * D * 2;
+        const bf16x8 ak = *(const bf16x8*)((const char*)kt + o);
+        const bf16x8 av = *(const bf16x8*)((const char*)vt + o);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s[mb], 0, 0, 0);
+        gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wf[ks], gg[mb], 0, 0, 0);
+      }
+    if (kv0 + BN - 1 > wave_kmin) {
+      const int lim = kmax - kv0 - 4 * half;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (mb * 32 + 8 * i + j > lim) s[mb][4 * i + j] = -INFINITY;
+    }
+    // dS = P (c1 + 2 c2 P + G), bf16 in the B-operand key order
+    bf16x8 dsf[PS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = fast_exp2(fmaf(c, s[mb][4 * i + j], neg_m));
+          const float dsv = pv * (fmaf(c2x2, pv, c1) + gg[mb][4 * i + j]);
+          dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
+        }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kst = 0; kst < PS; ++kst)
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(kt + t_off[0][dm] + kst * 16 * D));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(kt + t_off[1][dm] + kst * 16 * D));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dq[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kst], dq[dm], 0, 0, 0);
+      }
+  };
+
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) {
+      load_tile<D, BN, NW>(kb, (t + 1) * BN, voff, k_buf1, wave);
+      load_tile<D, BN, NW>(vb, (t + 1) * BN, voff, v_buf1, wave);
+    }
+    if (t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) {
+      load_tile<D, BN, NW>(kb, (t + 2) * BN, voff, k_buf0, wave);
+      load_tile<D, BN, NW>(vb, (t + 2) * BN, voff, v_buf0, wave);
+    }
+    if ((t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
+    __syncthreads();
+  }
+
+  if (!live) return;
+  const float ls = c * kLn2;  // lam * scale
+  float* out = p.dq + ri * D;
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(f32x4*)(out + dm * 32 + 8 * i + 4 * half) =
+          f32x4{dq[dm][4 * i] * ls, dq[dm][4 * i + 1] * ls, dq[dm][4 * i + 2] * ls, dq[dm][4 * i + 3] * ls};
+}
+
+// Which gradients a key-side kernel accumulates.
+constexpr int kBwdDkDv = 0, kBwdDk = 1, kBwdDv = 2;
+
+// dk/dv: a workgroup of NW waves owns 32 * NW keys of one (b, kv head); the query rows of
+// every head of the group stream through LDS in double-buffered tiles of BQ rows (q, w and
+// the row constants).  PART selects dk and dv, dk only, or dv only.
+template <int D, int BQ, int NW, int OCC, bool CAUSAL, int PART>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_bwd_dkdv_mfma_kernel(
+    const BwdMfmaParams p) {
+  constexpr bool DK = PART != kBwdDv;
+  constexpr bool DV = PART != kBwdDk;
+  constexpr int BK = NW * 32;
+  constexpr int MB = BQ / 32;
+  constexpr int KS = D / 16;
+  constexpr int DM = D / 32;
+  constexpr int PS = BQ / 16;
+  static_assert(BQ <= 64, "one wave-wide load brings the row constants of a tile");
+
+  __shared__ __attribute__((aligned(1024))) __bf16 q_buf0[BQ * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 q_buf1[BQ * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 w_buf0[BQ * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 w_buf1[BQ * D];
+  __shared__ __attribute__((aligned(1024))) f32x4 r_buf0[64];
+  __shared__ __attribute__((aligned(1024))) f32x4 r_buf1[64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const int bk = blockIdx.x / p.n_kt;  // b * Hkv + kv head
+  const int kt_i = blockIdx.x - bk * p.n_kt;
+  const int b = bk / p.Hkv;
+  const int hk = bk - b * p.Hkv;
+  const int G = p.H / p.Hkv;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int off = Tk - Tq;
+  const int key0 = kt_i * BK;
+  const int wk0 = key0 + wave * 32;
+  const int key = wk0 + col;
+  const bool live = key < Tk;
+  const size_t kr = (size_t)bk * Tk + key;
+
+  // K^T and V^T fragments (B operands): lane holds key `key`, dims ks * 16 + 8 * half + [0, 8)
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (live) {
+      kf[ks] = *(const bf16x8*)(p.k + kr * D + ks * 16 + 8 * half);
+      if constexpr (DK) vf[ks] = *(const bf16x8*)(p.v + kr * D + ks * 16 + 8 * half);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (__bf16)0.0f;
+    }
+  }
+
+  const uint32_t voff = tile_lane_offset<D, NW>(wave, lane);
+  const int q_x = half ^ chunk_swizzle<D>(col);
+  const uint32_t q_base = (uint32_t)(col * D * 2 + 16 * (q_x & 1));
+  const uint32_t q_xor = (uint32_t)(32 * (q_x >> 1));
+  const int gi = lane & 15;
+  const int g = lane >> 4;
+  int t_off[2][DM];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * half + (gi >> 2);
+    const int sw = chunk_swizzle<D>(row);
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+      const int lchunk = 4 * dm + 2 * (g & 1) + ((gi & 3) >> 1);
+      t_off[r][dm] = row * D + ((lchunk ^ sw) << 3) + 4 * (gi & 1);
+    }
+  }
+
+  f32x16 dk[DM], dv[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[dm][e] = dv[dm][e] = 0.0f;
+
+  // first query row that sees the workgroup's first key, and the wave's key range
+  const int i_begin = CAUSAL ? max(0, key0 - off) : 0;
+  const int t_begin = i_begin / BQ;
+  const int ntiles = (Tq + BQ - 1) / BQ;
+  const int wave_kmax = min(wk0 + 31, Tk - 1);
+
+  for (int gh = 0; gh < G; ++gh) {
+    const size_t bh = (size_t)b * p.H + hk * G + gh;
+    const uint32_t head_bytes = (uint32_t)((size_t)Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t qb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + bh * Tq * D), (short)0, head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.W + bh * Tq * D), (short)0, head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.R + bh * Tq), (short)0, (uint32_t)((size_t)Tq * 16), 0x00020000);
+    // rows past the end read as zero: q = w = 0 and (m, c1, c2, c) = 0 give P = 1, dS = 0
+    auto load = [&](int t, __bf16* qd, __bf16* wd, f32x4* rd) __attribute__((always_inline)) {
+      load_tile<D, BQ, NW>(qb, t * BQ, voff, qd, wave);
+      load_tile<D, BQ, NW>(wb, t * BQ, voff, wd, wave);
+      if (wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, POLAR_LDS(rd), 16, (uint32_t)((t * BQ + lane) * 16), 0, 0, 0);
+    };
+
+    auto compute_tile = [&](const __bf16* qt, const __bf16* wt, const f32x4* rt, int i0)
+                            __attribute__((always_inline)) {
+      f32x16 s[MB], gg[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] = gg[mb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint32_t o = (q_base + ((32u * ks) ^ q_xor)) + mb * 32 * D * 2;
+          const bf16x8 aq = *(const bf16x8*)((const char*)qt + o);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[mb], 0, 0, 0);
+          if constexpr (DK) {
+            const bf16x8 aw = *(const bf16x8*)((const char*)wt + o);
+            gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vf[ks], gg[mb], 0, 0, 0);
+          }
+        }
+      // causal: key j is visible to row i iff j <= i + off; only tiles whose first rows
+      // precede the wave's last key need the mask
+      const bool masked = CAUSAL && i0 + off < wave_kmax;
+      bf16x8 pf[PS], dsf[PS];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = mb * 32 + 8 * i + 4 * half + j;  // query row in the tile
+            const f32x4 rv = rt[r];
+            float x = s[mb][4 * i + j];
+            if (masked && key > i0 + r + off) x = -INFINITY;
+            const float pv = fast_exp2(fmaf(rv[3], x, -rv[0]));
+            if constexpr (DV) pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
+            if constexpr (DK) {
+              const float dsv = pv * (fmaf(2.0f * rv[2], pv, rv[1]) + gg[mb][4 * i + j]) * (rv[3] * kLn2);
+              dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
+            }
+          }
+      // dK^T += Q^T dS, dV^T += W^T P
+#pragma unroll
+      for (int kst = 0; kst < PS; ++kst)
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          if constexpr (DK) {
+            const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(qt + t_off[0][dm] + kst * 16 * D));
+            const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(qt + t_off[1][dm] + kst * 16 * D));
+            const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+            dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kst], dk[dm], 0, 0, 0);
+          }
+          if constexpr (DV) {
+            const s16x4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(wt + t_off[0][dm] + kst * 16 * D));
+            const s16x4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(wt + t_off[1][dm] + kst * 16 * D));
+            const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(wlo, whi, 0, 1, 2, 3, 4, 5, 6, 7));
+            dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, pf[kst], dv[dm], 0, 0, 0);
+          }
+        }
+    };
+
+    if (t_begin >= ntiles) continue;  // no query row sees these keys (uniform)
+    __syncthreads();  // the previous head's last tile is no longer read
+    load(t_begin, q_buf0, w_buf0, r_buf0);
+    __syncthreads();
+    for (int t = t_begin; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load(t + 1, q_buf1, w_buf1, r_buf1);
+      if (!CAUSAL || t * BQ + BQ - 1 + off >= wk0) compute_tile(q_buf0, w_buf0, r_buf0, t * BQ);
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) load(t + 2, q_buf0, w_buf0, r_buf0);
+      if (!CAUSAL || (t + 1) * BQ + BQ - 1 + off >= wk0) compute_tile(q_buf1, w_buf1, r_buf1, (t + 1) * BQ);
+      __syncthreads();
+    }
+  }
+
+  if (!live) return;
+  float* ok = p.dk + kr * D;
+  float* ov = p.dv + kr * D;
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DK)
+        *(f32x4*)(ok + dm * 32 + 8 * i + 4 * half) =
+            f32x4{dk[dm][4 * i], dk[dm][4 * i + 1], dk[dm][4 * i + 2], dk[dm][4 * i + 3]};
+      if constexpr (DV)
+        *(f32x4*)(ov + dm * 32 + 8 * i + 4 * half) =
+            f32x4{dv[dm][4 * i], dv[dm][4 * i + 1], dv[dm][4 * i + 2], dv[dm][4 * i + 3]};
+    }
+}
+
+}  // namespace polar

@@ -10,6 +10,7 @@
 
 #include "../../include/polar_attn.h"
 #include "bwd.h"
+#include "bwd_mfma.h"
 #include "decode.h"
 #include "decode_group.h"
 #include "fwd_bf16.h"
@@ -412,8 +413,57 @@ polar_status merge_with_lens(const polar_problem* pr, const float* partials, int
 
 // ---- backward
 
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Backward workspace.  fp32 inputs: w and the row constants in fp32, [rows, D + 4].
+// bf16 inputs: the forward's partial rows [rows, D + 3] fp32, then w as bf16 [rows, D],
+// then the row constants [rows] f32x4, each part starting on a 256-byte boundary.
 size_t bwd_workspace(const polar_problem* pr) {
-  return (size_t)pr->batch * pr->heads * pr->seq_q * (pr->head_dim + 4) * sizeof(float);
+  const size_t rows = (size_t)pr->batch * pr->heads * pr->seq_q;
+  const size_t D = pr->head_dim;
+  if (pr->dtype == POLAR_F32) return rows * (D + 4) * sizeof(float);
+  if (rows == 0) return 0;
+  return align256(rows * (D + 3) * 4) + align256(rows * D * 2) + rows * 16;
+}
+
+constexpr int kBwdWaves = 4;  // matrix-core backward: 32 rows (or keys) per wave
+
+// bf16 backward on the matrix cores: the forward in partial mode for the row statistics,
+// then the row constants, dq and dk/dv.
+template <int D, bool CAUSAL>
+polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdMfmaParams& mp, void* stream) {
+  polar_status st = POLAR_OK;
+  if (mp.Tq > 0) {
+    st = launch_fwd<D, CAUSAL>(pr, fp, stream);
+    if (st != POLAR_OK) return st;
+    const long long rows = (long long)mp.B * mp.H * mp.Tq;
+    if ((rows + 3) / 4 > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+    st = launch(polar::polar_bwd_prep_kernel<D, CAUSAL>, dim3((unsigned)((rows + 3) / 4)), dim3(256), mp, stream);
+    if (st != POLAR_OK) return st;
+    mp.n_qt = (mp.Tq + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
+    const long long qblocks = (long long)mp.n_qt * mp.B * mp.H;
+    if (qblocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+    st = launch(polar::polar_bwd_dq_mfma_kernel<D, 64, kBwdWaves, CAUSAL>, dim3((unsigned)qblocks),
+                dim3(kBwdWaves * 64), mp, stream);
+    if (st != POLAR_OK) return st;
+  }
+  // with no query rows this writes zero dk and dv
+  mp.n_kt = (mp.Tk + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
+  const long long kblocks = (long long)mp.n_kt * mp.B * mp.Hkv;
+  if (kblocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+  // d = 64: dk and dv in one kernel with 32-row query tiles; d = 128: a dk kernel with
+  // 32-row tiles and a dv kernel with 64-row tiles; all at 2 waves per SIMD
+  const dim3 grid((unsigned)kblocks), block(kBwdWaves * 64);
+  if constexpr (D == 64) {
+    return launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv>, grid, block, mp,
+                  stream);
+  } else {
+    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDk>, grid, block, mp,
+                stream);
+    if (st != POLAR_OK) return st;
+    return launch(polar::polar_bwd_dkdv_mfma_kernel<D, 64, kBwdWaves, 2, CAUSAL, polar::kBwdDv>, grid, block, mp,
+                  stream);
+  }
 }
 
 template <int D, typename T, bool CAUSAL>
@@ -691,8 +741,8 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   if (st != POLAR_OK) return st;
   if (!g) return POLAR_ERR_NULL_ARG;
   if (pr->batch == 0) return POLAR_OK;  // nothing to write
-  // the grid's second dimension holds (batch, head) pairs
-  if ((int64_t)pr->batch * pr->heads > 65535) return POLAR_ERR_UNSUPPORTED;
+  // fp32 path: the grid's second dimension holds (batch, head) pairs
+  if (pr->dtype == POLAR_F32 && (int64_t)pr->batch * pr->heads > 65535) return POLAR_ERR_UNSUPPORTED;
   const bool rows = pr->seq_q > 0;
   const size_t ws = bwd_workspace(pr);
   if (!k || !v || !dk || !dv) return POLAR_ERR_NULL_ARG;
@@ -718,6 +768,57 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
     for (int o2 = o + 1; o2 < 4; ++o2)
       if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return POLAR_ERR_ALIAS;
   }
+  if (pr->dtype == POLAR_BF16) {
+    const size_t part_b = align256(nq * (D + 3) * 4);
+    const size_t w_b = align256(nq * D * 2);
+    char* base = static_cast<char*>(workspace);
+    polar::BwdMfmaParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    mp.q = static_cast<const __bf16*>(q);
+    mp.k = static_cast<const __bf16*>(k);
+    mp.v = static_cast<const __bf16*>(v);
+    mp.part = rows ? reinterpret_cast<const float*>(base) : nullptr;
+    mp.g_dir = g->d_direction;
+    mp.g_neff = g->d_n_eff;
+    mp.g_conf = g->d_confidence;
+    mp.g_count = g->d_count;
+    mp.W = rows ? reinterpret_cast<__bf16*>(base + part_b) : nullptr;
+    mp.R = rows ? reinterpret_cast<polar::f32x4*>(base + part_b + w_b) : nullptr;
+    mp.dq = dq;
+    mp.dk = dk;
+    mp.dv = dv;
+    mp.B = pr->batch;
+    mp.H = pr->heads;
+    mp.Hkv = pr->kv_heads;
+    mp.Tq = pr->seq_q;
+    mp.Tk = pr->seq_k;
+    mp.floor_on = bp.floor_on;
+    mp.hp_stride = bp.hp_stride;
+    mp.scale = bp.scale;
+    mp.hp = bp.hp;
+    // the forward in partial mode writes every row's (m, S1, S2, acc) into the workspace
+    FwdParams fp;
+    std::memset(&fp, 0, sizeof(fp));
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.part = reinterpret_cast<float*>(base);
+    fp.part_S = 1;
+    fp.part_s = 0;
+    fp.B = pr->batch;
+    fp.H = pr->heads;
+    fp.Hkv = pr->kv_heads;
+    fp.Tq = pr->seq_q;
+    fp.Tk = pr->seq_k;
+    fp.floor_on = bp.floor_on;
+    fp.hp_stride = bp.hp_stride;
+    fp.scale = bp.scale;
+    fp.hp = bp.hp;
+    if (pr->head_dim == 64)
+      return pr->causal ? launch_bwd_mfma<64, true>(pr, fp, mp, stream) : launch_bwd_mfma<64, false>(pr, fp, mp, stream);
+    return pr->causal ? launch_bwd_mfma<128, true>(pr, fp, mp, stream)
+                      : launch_bwd_mfma<128, false>(pr, fp, mp, stream);
+  }
   bp.q = q;
   bp.k = k;
   bp.v = v;
@@ -735,7 +836,7 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   bp.Hkv = pr->kv_heads;
   bp.Tq = pr->seq_q;
   bp.Tk = pr->seq_k;
-  return pr->dtype == POLAR_F32 ? dispatch_bwd<float>(pr, bp, stream) : dispatch_bwd<__bf16>(pr, bp, stream);
+  return dispatch_bwd<float>(pr, bp, stream);
 }
 
 }  // extern "C"

@@ -299,8 +299,14 @@ def test_fwd_partial_validation(lib):
 def test_bwd_validation(lib):
     prob = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128)
     pr, keep = prob.to_c()
-    ws = 2 * 4 * 48 * (128 + 4) * 4
+    rows = 2 * 4 * 48
+    up = lambda x: (x + 255) // 256 * 256
+    # bf16: forward statistics (d + 3 fp32), w (d bf16), row constants (4 fp32), 256-byte parts
+    ws = up(rows * 131 * 4) + up(rows * 128 * 2) + rows * 16
     assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr)) == ws
+    pr32, keep32 = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128,
+                                dtype=pa.POLAR_F32).to_c()
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr32)) == rows * (128 + 4) * 4
     bad, keep2 = good_problem(head_dim=96).to_c()
     assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(bad)) == 0
     g = pa.PolarGrads(fake(20), fake(21), None, fake(22))
@@ -335,8 +341,8 @@ def test_bwd_validation(lib):
     rows0, keep5 = good_problem(seq_q=0).to_c()
     assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(rows0)) == 0
     assert run(problem=rows0, dk=None, q=None, dq=None, work=None, nbytes=0) == 1
-    # the (batch, head) grid dimension is limited to 65535 pairs
-    big, keep6 = good_problem(batch=40000, heads=2, kv_heads=2).to_c()
+    # the fp32 path's (batch, head) grid dimension is limited to 65535 pairs
+    big, keep6 = good_problem(batch=40000, heads=2, kv_heads=2, dtype=pa.POLAR_F32).to_c()
     assert run(problem=big) == 3
 
 

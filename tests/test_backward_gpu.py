@@ -1,13 +1,18 @@
 """GPU parity of the backward (polar_attn_bwd) against the fp64 gradient oracle.
 
-Both sides see the same input values (bf16 inputs widened exactly); the kernels compute
-in fp32, the oracle in fp64.  Metric, per output tensor: max |gpu - oracle| over the
-tensor divided by max |oracle|.  Every output element is an fp32 sum over at most n
-visible terms (keys for dq, query rows times the group for dk and dv) of products whose
-size the largest output bounds, so its error stays within a small multiple of
-n * 2^-24: BWD_TOL = 1e-4 for the cases here (n <= 1200), BWD_TOL_16K = 1e-3 at 16384
-keys.  A tensor whose exact gradient is zero (no upstream gradient reaches it) must come
-back exactly zero.
+Both sides see the same input values (bf16 inputs widened exactly); the oracle computes
+in fp64.  Metric, per output tensor: max |gpu - oracle| over the tensor divided by
+max |oracle|.
+  fp32 inputs: the kernels compute in fp32; every output element is an fp32 sum over at
+    most n visible terms (keys for dq, query rows times the group for dk and dv) of
+    products whose size the largest output bounds, so its error stays within a small
+    multiple of n * 2^-24: BWD_TOL = 1e-4 for the cases here (n <= 1200).
+  bf16 inputs: the matrix-core path rounds P, dS and w to bf16 (relative 2^-9 each) and
+    takes the row statistics from the bf16 forward (n_eff within 1e-2), so an output is
+    off by a few times 2^-9 of the largest one: BWD_TOL_BF16 = 2e-2, the forward's bound
+    for the direction.
+A tensor whose exact gradient is zero (no upstream gradient reaches it) must come back
+exactly zero.
 """
 import numpy as np
 import pytest
@@ -22,11 +27,11 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 BWD_TOL = 1e-4
-BWD_TOL_16K = 1e-3
+BWD_TOL_BF16 = 2e-2
 ALL = ("direction", "n_eff", "confidence", "count")
 
 
-def compare(out, ref, label):
+def compare(out, ref, label, tol=BWD_TOL):
     errs = {}
     for key in ("dq", "dk", "dv"):
         g, r = to_np(out[key]), ref[key]
@@ -38,7 +43,7 @@ def compare(out, ref, label):
             errs[key] = 0.0
             continue
         errs[key] = float(np.abs(g - r).max() / top)
-        assert errs[key] <= BWD_TOL, f"{label} {key}: {errs[key]:.3e} > {BWD_TOL:.0e} ({errs})"
+        assert errs[key] <= tol, f"{label} {key}: {errs[key]:.3e} > {tol:.0e} ({errs})"
     print(f"[bwd] {label} {errs}", flush=True)
     return errs
 
@@ -54,7 +59,7 @@ def bwd_case(B, H, Hkv, Tq, Tk, d, dtype, causal, seed, tau=None, beta=None, kap
     out = pa.bwd(q.to(DEV), k.to(DEV), v.to(DEV), {n: t.to(DEV) for n, t in gr.items()}, causal=causal,
                  len_temp=tau, null_bias=beta, count_scale=kappa, softmax_scale=scale)
     torch.cuda.synchronize()
-    return compare(out, ref, label)
+    return compare(out, ref, label, BWD_TOL if dtype == torch.float32 else BWD_TOL_BF16)
 
 
 TAU4 = [0.05, 0.0, 0.2, 0.1]
@@ -155,14 +160,16 @@ def test_workload_backward_16k():
         got = dq[0, h, i].numpy()
         err = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
         print(f"[bwd] workload dq row h={h} i={i}: {err:.2e}", flush=True)
-        assert err <= BWD_TOL_16K, (h, i, err)
+        assert err <= BWD_TOL_BF16, (h, i, err)
     qd, kd, vd = q.double(), k.double(), v.double()
     for hk in range(w.Hkv):
         heads = slice(hk * group, (hk + 1) * group)
         sv = float((vd[0, hk] * dv[0, hk]).sum())
         sv_abs = float((vd[0, hk] * dv[0, hk]).abs().sum())
-        assert abs(sv) <= 1e-4 * sv_abs, (hk, sv, sv_abs)
+        print(f"[bwd] workload identities hk={hk}: v.dv {abs(sv) / sv_abs:.2e}", flush=True)
+        assert abs(sv) <= BWD_TOL_BF16 * sv_abs, (hk, sv, sv_abs)
         lhs = float((qd[0, heads] * dq[0, heads]).sum())
         rhs = float((kd[0, hk] * dk[0, hk]).sum())
         scale = float((qd[0, heads] * dq[0, heads]).abs().sum())
-        assert abs(lhs - rhs) <= 1e-4 * scale, (hk, lhs, rhs, scale)
+        print(f"[bwd] workload identities hk={hk}: q.dq - k.dk {abs(lhs - rhs) / scale:.2e}", flush=True)
+        assert abs(lhs - rhs) <= BWD_TOL_BF16 * scale, (hk, lhs, rhs, scale)
