@@ -43,29 +43,32 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
 # Sources each profiled kernel is built from (besides the shared header, the ABI header
-# and the launch-geometry constants of the host file).
+# and the launch-geometry constants of the host file), and the kernel's name, whose
+# template arguments in the host file's dispatch lines are part of its build.
 KERNEL_SOURCES = {
-    "fwd_bf16_t65536_d64": ["fwd_bf16.h"],
-    "fwd_bf16_t16384_d128": ["fwd_bf16.h"],
-    "decode_b64_h8_tk65536_d128": ["decode.h"],
-    "merge_b64_h8_d128": ["decode.h"],
-    "paged_gqa_decode_b64_h32_kv8_tk65536_d128": ["decode_group.h", "decode.h"],
-    "bwd_dq_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
-    "bwd_dk_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
-    "bwd_dv_b1_h16_kv4_t16384_d128": ["bwd_mfma.h", "bwd.h", "fwd_bf16.h"],
+    "fwd_bf16_t65536_d64": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
+    "fwd_bf16_t16384_d128": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
+    "decode_b64_h8_tk65536_d128": (["decode.h"], "polar_decode_split_kernel"),
+    "merge_b64_h8_d128": (["decode.h"], "polar_merge_kernel"),
+    "paged_gqa_decode_b64_h32_kv8_tk65536_d128": (["decode_group.h", "decode.h"], "polar_decode_group_kernel"),
+    "bwd_dq_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dq_mfma_kernel"),
+    "bwd_dk_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
+    "bwd_dv_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
 }
 
 
 def source_digest(kernel_key=None):
     """Digest of the sources a kernel is built from: its headers, polar_common.h, the ABI
-    header and the launch-geometry lines of polar_attn.hip (all of csrc/ when no kernel
-    is named).  A profile stays valid while this digest is unchanged."""
+    header, the launch-geometry lines of polar_attn.hip and its lines that name the kernel
+    (all of csrc/ when no kernel is named).  A profile stays valid while this digest is
+    unchanged."""
     csrc = os.path.join(ROOT, "long_context_attention_polar_amd", "csrc")
     h = hashlib.sha256()
     if kernel_key is None:
         names = sorted(os.listdir(csrc))
     else:
-        names = sorted(set(KERNEL_SOURCES[kernel_key]) | {"polar_common.h"})
+        headers, kernel = KERNEL_SOURCES[kernel_key]
+        names = sorted(set(headers) | {"polar_common.h"})
     for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
@@ -73,8 +76,8 @@ def source_digest(kernel_key=None):
         with open(os.path.join(ROOT, "include", "polar_attn.h"), "rb") as f:
             h.update(f.read())
         with open(os.path.join(csrc, "polar_attn.hip")) as f:
-            geometry = [ln for ln in f if ln.lstrip().startswith(("constexpr int k", "#define POLAR_"))]
-        h.update("".join(geometry).encode())
+            host = [ln for ln in f if ln.lstrip().startswith(("constexpr int k", "#define POLAR_")) or kernel in ln]
+        h.update("".join(host).encode())
     return h.hexdigest()[:16]
 
 

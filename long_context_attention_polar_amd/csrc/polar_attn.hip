@@ -294,7 +294,7 @@ polar_status launch_group_kf(int chunk, polar::GroupDecodeParams& gp, dim3 grid,
     case 2:
       return launch(polar::polar_decode_group_kernel<D, 2, NW, 4, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
     case 4:
-      return launch(polar::polar_decode_group_kernel<D, 4, NW, 2, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
+      return launch(polar::polar_decode_group_kernel<D, 4, NW, 4, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
     default:
       return launch(polar::polar_decode_group_kernel<D, 8, NW, 2, PAGED, KF>, grid, dim3(NW * 64), gp, stream);
   }
