@@ -106,9 +106,9 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int key = base + slot + u * NSLOT;
-      if (key < hi) {
-        kr[u] = *(const u32x4*)(kb + (size_t)key * D + dch * 8);
-        vr[u] = *(const u32x4*)(vb + (size_t)key * D + dch * 8);
+      if (key < hi) {  // each cache byte is read once: non-temporal loads
+        kr[u] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)key * D + dch * 8));
+        vr[u] = __builtin_nontemporal_load((const u32x4*)(vb + (size_t)key * D + dch * 8));
       } else {
         kr[u] = u32x4{0, 0, 0, 0};
         vr[u] = u32x4{0, 0, 0, 0};

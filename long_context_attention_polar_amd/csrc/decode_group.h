@@ -136,8 +136,8 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const Group
       }
       if (ok[u]) {
         const size_t off = (PAGED ? row * D : cont_off + row * D) + dch * 8;
-        kr[u] = *(const u32x4*)(kbase + off);
-        vr[u] = *(const u32x4*)(vbase + off);
+        kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));  // read once
+        vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
       } else {
         kr[u] = u32x4{0, 0, 0, 0};
         vr[u] = u32x4{0, 0, 0, 0};
