@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,11 +58,19 @@ KERNEL_SOURCES = {
 }
 
 
+def _code(text):
+    """Source text without comments and blank space, so that edits of the documentation
+    leave a digest unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel_key=None):
-    """Digest of the sources a kernel is built from: its headers, polar_common.h, the ABI
+    """Digest of the code a kernel is built from: its headers, polar_common.h, the ABI
     header, the launch-geometry lines of polar_attn.hip and its lines that name the kernel
-    (all of csrc/ when no kernel is named).  A profile stays valid while this digest is
-    unchanged."""
+    (all of csrc/ when no kernel is named), comments excluded.  A profile stays valid
+    while this digest is unchanged."""
     csrc = os.path.join(ROOT, "long_context_attention_polar_amd", "csrc")
     h = hashlib.sha256()
     if kernel_key is None:
@@ -70,15 +79,21 @@ def source_digest(kernel_key=None):
         headers, kernel = KERNEL_SOURCES[kernel_key]
         names = sorted(set(headers) | {"polar_common.h"})
     for name in names:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update((name + _code(f.read())).encode())
     if kernel_key is not None:
-        with open(os.path.join(ROOT, "include", "polar_attn.h"), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "include", "polar_attn.h")) as f:
+            h.update(_code(f.read()).encode())
         with open(os.path.join(csrc, "polar_attn.hip")) as f:
-            host = [ln for ln in f if ln.lstrip().startswith(("constexpr int k", "#define POLAR_")) or kernel in ln]
-        h.update("".join(host).encode())
+            host = [ln for ln in _code_lines(f.read())
+                    if ln.startswith(("constexpr int k", "#define POLAR_")) or kernel in ln]
+        h.update("\n".join(host).encode())
     return h.hexdigest()[:16]
+
+
+def _code_lines(text):
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return [" ".join(re.sub(r"//.*", "", ln).split()) for ln in text.split("\n")]
 
 
 def prefill_flops(w):

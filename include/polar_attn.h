@@ -174,7 +174,8 @@ typedef struct polar_outputs {
  * One pass over the visible keys per query tile: tiled Q K^T and P V on the matrix
  * cores with an online softmax that also streams sum p^2 (rescaled by the square of
  * each correction factor).  Supports bf16 and fp32, head_dim 64 and 128, causal and
- * non-causal, seq_q <= seq_k when causal (rows aligned to the end of the keys). */
+ * non-causal, seq_q <= seq_k when causal (rows aligned to the end of the keys).  Every
+ * reading variant (a sliding window needs causal). */
 polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const void* k,
                             const void* v, const polar_outputs* out, void* stream);
 
@@ -191,7 +192,10 @@ polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const v
  * into exactly what one pass over the whole context computes; merge them with a
  * problem of seq_k = context_k, causal.  context_k = 0 uses the row's own visible count.
  * Requires context_k >= seq_q when nonzero and 1 + tau_h ln(context_k) > 0.  Slots other
- * than `split` are not touched; a slot that never receives a piece must hold m = -inf. */
+ * than `split` are not touched; a slot that never receives a piece must hold m = -inf.
+ * Reading variants: all but a sliding window and POLAR_LEVEL_QNORM (the merge that
+ * finishes the pieces has no queries); a per-key floor uses the floor of the row's count
+ * in the whole context. */
 polar_status polar_attn_fwd_partial(const polar_problem* problem, const void* q, const void* k, const void* v,
                                     int32_t context_k, float* partials, int32_t num_splits, int32_t split,
                                     void* stream);
@@ -211,7 +215,8 @@ size_t polar_attn_decode_workspace_bytes(const polar_problem* problem, int32_t n
  * as for polar_attn_merge), and a second kernel on the same stream merges them with
  * the global visible count n = seq_k.  1 <= num_splits <= seq_k, or 0 for automatic.
  * When heads > kv_heads, a workgroup serves up to 8 query heads of a group and reads
- * each K and V row once for all of them. */
+ * each K and V row once for all of them.  Every reading variant; a sliding window of W
+ * keys keeps the last min(W, seq_k) keys (n = that count). */
 polar_status polar_attn_decode(const polar_problem* problem, const void* q, const void* k_cache,
                                const void* v_cache, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, const polar_outputs* out, void* stream);
@@ -251,7 +256,8 @@ size_t polar_attn_decode_paged_workspace_bytes(const polar_problem* problem, con
  * workgroup serves a (sequence, KV head, split) and up to 8 query heads of the group,
  * loading each K and V row once for all of them.  Writes the same per-split partials
  * as polar_attn_decode into `workspace` ([batch, heads, S, head_dim + 3] fp32) and then
- * merges them on the same stream. */
+ * merges them on the same stream.  Every reading variant; a sliding window of W keys
+ * keeps the last min(W, length) keys of each sequence (n = that count). */
 polar_status polar_attn_decode_paged(const polar_problem* problem, const void* q, const polar_paged_kv* kv,
                                      int32_t num_splits, void* workspace, size_t workspace_bytes,
                                      const polar_outputs* out, void* stream);
@@ -262,7 +268,9 @@ polar_status polar_attn_decode_paged(const polar_problem* problem, const void* q
  * exp(m); a split with no keys has m = -inf.  Each split is brought to the common
  * maximum m* with w = exp(m_s - m*) (S1 and acc scale by w, S2 by w^2), then the
  * channels are formed with the visible count of the problem's row i (seq_k when not
- * causal, i + 1 + seq_k - seq_q when causal).  dtype is ignored. */
+ * causal, i + 1 + seq_k - seq_q when causal; min(W, that count) under a sliding window of
+ * W keys).  dtype is ignored.  Reading variants: all but POLAR_LEVEL_QNORM, which needs
+ * the queries (POLAR_ERR_UNSUPPORTED). */
 polar_status polar_attn_merge(const polar_problem* problem, const float* partials,
                               int32_t num_splits, const polar_outputs* out, void* stream);
 
