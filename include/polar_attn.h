@@ -288,8 +288,12 @@ typedef struct polar_grads {
 /* Bytes of device workspace polar_attn_bwd needs.  fp32 inputs: B * heads * seq_q *
  * (head_dim + 4) fp32 (per query row, the vector w and four row constants).  bf16 inputs:
  * per query row the forward's statistics (head_dim + 3 fp32), w (head_dim bf16) and four
- * row constants (fp32), in three parts each padded to 256 bytes.  0 when the problem is
- * invalid (or has no query rows). */
+ * row constants (fp32), in three parts each padded to 256 bytes; then, when the key
+ * side's work is split into n > 1 runs per 128-key tile, n partial dk and n partial dv
+ * (n * B * kv_heads * seq_k * head_dim fp32 each, padded to 256 bytes).  n depends on the
+ * shape only: for B * kv_heads * ceil(seq_k / 128) = t key tiles, n = ceil(2048 / t)
+ * (causal) or ceil(512 / t) (full mask), clamped to [1, 4 * heads / kv_heads].  0 when
+ * the problem is invalid (or has no query rows). */
 size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
 
 /* Backward of polar_attn_fwd: the gradients of
@@ -317,7 +321,8 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
  * scratch owned by the call until the stream reaches its end.  No output or the
  * workspace may overlap an input or another output.  batch == 0 enqueues nothing;
  * seq_q == 0 (q, dq and workspace may then be NULL) writes zero dk and dv.  The kernels
- * (three for fp32, four for bf16) run in order on `stream`. */
+ * (three for fp32; four to six for bf16, the last summing split partial dk and dv in a
+ * fixed order, so results are deterministic) run in order on `stream`. */
 polar_status polar_attn_bwd(const polar_problem* problem, const void* q, const void* k, const void* v,
                             const polar_grads* grads, float* dq, float* dk, float* dv, void* workspace,
                             size_t workspace_bytes, void* stream);

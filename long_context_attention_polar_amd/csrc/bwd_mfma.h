@@ -6,18 +6,22 @@
 // layouts of the bf16 forward kernel:
 //   rows   the forward kernel in partial mode gives every row's (m, S1, S2, acc); a small
 //          kernel turns them and the upstream gradients into w (bf16) and the row
-//          constants (m in base 2, c1, c2, c);
+//          constants (m in base 2, c, cl c1, 2 cl c2) with cl = lam scale, the factor that
+//          dq and dk carry, so both take cl dS = P (cl c1 + 2 cl c2 P + cl G);
 //   dq     per query tile: S^T = K Q^T and G^T = V W^T (K, V rows from LDS, Q and W in
-//          registers, lane = query); dS = P (c1 + 2 c2 P + G) on the vector ALUs, rounded
-//          to bf16 in the B-operand key order; dQ^T += K^T dS^T with K^T read from the
-//          row-major K tile by transpose reads;
+//          registers, lane = query); cl dS on the vector ALUs, rounded to bf16 in the
+//          B-operand key order; dQ^T += K^T (cl dS)^T with K^T read from the row-major K
+//          tile by transpose reads;
 //   dk/dv  per key tile, over the query rows of every query head of its GQA group:
 //          S = Q K^T and G = W V^T (Q, W rows from LDS, K and V in registers, lane = key);
-//          P and dS with the per-row constants read from LDS; dK^T += Q^T dS and
+//          P and cl dS with the per-row constants read from LDS; dK^T += Q^T (cl dS) and
 //          dV^T += W^T P with Q^T and W^T from transpose reads.  At d = 128 the four
 //          accumulators and the K, V fragments do not fit one wave's share of two waves per
 //          SIMD, so dk (S, G, dK) and dv (S, dV) run as two kernels that each keep two
-//          waves per SIMD; S is computed in both.
+//          waves per SIMD; S is computed in both.  Under a causal mask the first key
+//          tiles see ~Tq/128 times the query rows of the last, so a key tile's (head,
+//          query tile) pairs may be cut into runs of one workgroup each, whose partial
+//          dk and dv a last kernel adds in run order.
 // P, dS and w enter the products as bf16 (round to nearest even); every sum is fp32.
 #pragma once
 
@@ -36,13 +40,17 @@ struct BwdMfmaParams {
   const float* g_conf;
   const float* g_count;
   __bf16* W;             // [B, H, Tq, D]: w of every row, bf16
-  f32x4* R;              // [B, H, Tq]: (m in base 2, c1, c2, c = lam scale log2 e)
+  f32x4* R;              // [B, H, Tq]: (m in base 2, c = lam scale log2 e, cl c1, 2 cl c2), cl = lam scale
   float* dq;             // [B, H, Tq, D]
   float* dk;             // [B, Hkv, Tk, D]
   float* dv;
   int B, H, Hkv, Tq, Tk;
   int n_qt;              // query tiles per (b, h) of the dq kernel
   int n_kt;              // key tiles per (b, kv head) of the dk/dv kernel
+  int n_split;           // workgroups per key tile of the dk/dv kernel (1: no partial sums)
+  float* dk_part;        // n_split > 1: [n_split, B, Hkv, Tk, D] partial dk, then dv alike
+  float* dv_part;
+  long long part_n4;     // B * Hkv * Tk * D / 4: f32x4 elements of dk (and of dv)
   int floor_on;
   int hp_stride;
   float scale;
@@ -87,7 +95,11 @@ __global__ __launch_bounds__(256) void polar_bwd_prep_kernel(const BwdMfmaParams
     float c1, c2;
     row_constants(p.hp, hpi, p.floor_on != 0, n, lam, m_nat, pr[1], pr[2], p.g_neff ? p.g_neff[row] : 0.0f,
                   p.g_conf ? p.g_conf[row] : 0.0f, p.g_count ? p.g_count[row] : 0.0f, c1, c2);
-    p.R[row] = f32x4{m_nat * kLog2e, c1, c2, logit_scale(lam, p.scale)};
+    // the products take dS scaled by cl = lam scale, the factor dq and dk carry:
+    // cl dS = p (cl c1 + 2 cl c2 p + cl <w, v>)
+    const float c = logit_scale(lam, p.scale);
+    const float cl = c * kLn2;
+    p.R[row] = f32x4{m_nat * kLog2e, c, cl * c1, 2.0f * cl * c2};
   }
 }
 
@@ -144,8 +156,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int kmax = CAUSAL ? min(qrow + off, Tk - 1) : Tk - 1;
   const size_t ri = (size_t)bh * Tq + qrow;
   // a row past the end gets weight 0 everywhere (m = +inf); its output is never written
-  const f32x4 rv = live ? p.R[ri] : f32x4{INFINITY, 0.0f, 0.0f, 1.0e-30f};
-  const float neg_m = -rv[0], c1 = rv[1], c2x2 = 2.0f * rv[2], c = rv[3];
+  const f32x4 rv = live ? p.R[ri] : f32x4{INFINITY, 1.0e-30f, 0.0f, 0.0f};
+  const float neg_m = -rv[0], c = rv[1], cc1 = rv[2], cc2 = rv[3], cl = c * kLn2;
 
   // Q^T and W^T fragments: lane holds row qrow, dims ks * 16 + 8 * half + [0, 8)
   bf16x8 qf[KS], wf[KS];
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           for (int j = 0; j < 4; ++j)
             if (mb * 32 + 8 * i + j > lim) s[mb][4 * i + j] = -INFINITY;
     }
-    // dS = P (c1 + 2 c2 P + G), bf16 in the B-operand key order
+    // cl dS = P (cl c1 + 2 cl c2 P + cl G), bf16 in the B-operand key order
     bf16x8 dsf[PS];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float pv = fast_exp2(fmaf(c, s[mb][4 * i + j], neg_m));
-          const float dsv = pv * (fmaf(c2x2, pv, c1) + gg[mb][4 * i + j]);
+          const float dsv = pv * fmaf(cc2, pv, fmaf(cl, gg[mb][4 * i + j], cc1));
           dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
         }
     // dQ^T += K^T dS^T
@@ -255,14 +267,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   if (!live) return;
-  const float ls = c * kLn2;  // lam * scale
   float* out = p.dq + ri * D;
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *(f32x4*)(out + dm * 32 + 8 * i + 4 * half) =
-          f32x4{dq[dm][4 * i] * ls, dq[dm][4 * i + 1] * ls, dq[dm][4 * i + 2] * ls, dq[dm][4 * i + 3] * ls};
+          f32x4{dq[dm][4 * i], dq[dm][4 * i + 1], dq[dm][4 * i + 2], dq[dm][4 * i + 3]};
 }
 
 // Which gradients a key-side kernel accumulates.
@@ -296,8 +307,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  const int bk = blockIdx.x / p.n_kt;  // b * Hkv + kv head
-  const int kt_i = blockIdx.x - bk * p.n_kt;
+  // blockIdx = (key tile * B * Hkv + (b * Hkv + kv head)) * n_split + split: the key tiles
+  // that the most query rows see come first
+  const int nbk = p.B * p.Hkv;
+  const int sp = blockIdx.x % p.n_split;
+  const int kb_i = blockIdx.x / p.n_split;
+  const int kt_i = kb_i / nbk;
+  const int bk = kb_i - kt_i * nbk;  // b * Hkv + kv head
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
   const int G = p.H / p.Hkv;
@@ -348,11 +364,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 
   // first query row that sees the workgroup's first key, and the wave's key range
   const int i_begin = CAUSAL ? max(0, key0 - off) : 0;
-  const int t_begin = i_begin / BQ;
-  const int ntiles = (Tq + BQ - 1) / BQ;
+  const int t_begin = min(i_begin / BQ, (Tq + BQ - 1) / BQ);
+  const int nt_vis = (Tq + BQ - 1) / BQ - t_begin;  // query tiles per head that see the keys
   const int wave_kmax = min(wk0 + 31, Tk - 1);
+  // the (head, query tile) pairs of the key tile, head-major, cut into n_split contiguous
+  // runs of near-equal length; this workgroup takes run sp
+  const long long items = (long long)G * nt_vis;
+  const long long it_lo = items * sp / p.n_split;
+  const long long it_hi = items * (sp + 1) / p.n_split;
 
   for (int gh = 0; gh < G; ++gh) {
+    const int t_lo = t_begin + (int)max(it_lo - (long long)gh * nt_vis, 0ll);
+    const int ntiles = t_begin + (int)min(it_hi - (long long)gh * nt_vis, (long long)nt_vis);
     const size_t bh = (size_t)b * p.H + hk * G + gh;
     const uint32_t head_bytes = (uint32_t)((size_t)Tq * D * 2);
     const __amdgpu_buffer_rsrc_t qb =
@@ -361,7 +384,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.W + bh * Tq * D), (short)0, head_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.R + bh * Tq), (short)0, (uint32_t)((size_t)Tq * 16), 0x00020000);
-    // rows past the end read as zero: q = w = 0 and (m, c1, c2, c) = 0 give P = 1, dS = 0
+    // rows past the end read as zero: q = w = 0 and zero row constants give P = 1, dS = 0
     auto load = [&](int t, __bf16* qd, __bf16* wd, f32x4* rd) __attribute__((always_inline)) {
       load_tile<D, BQ, NW>(qb, t * BQ, voff, qd, wave);
       load_tile<D, BQ, NW>(wb, t * BQ, voff, wd, wave);
@@ -402,10 +425,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             const f32x4 rv = rt[r];
             float x = s[mb][4 * i + j];
             if (masked && key > i0 + r + off) x = -INFINITY;
-            const float pv = fast_exp2(fmaf(rv[3], x, -rv[0]));
+            const float pv = fast_exp2(fmaf(rv[1], x, -rv[0]));
             if constexpr (DV) pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
             if constexpr (DK) {
-              const float dsv = pv * (fmaf(2.0f * rv[2], pv, rv[1]) + gg[mb][4 * i + j]) * (rv[3] * kLn2);
+              const float dsv = pv * fmaf(rv[3], pv, fmaf(rv[1] * kLn2, gg[mb][4 * i + j], rv[2]));
               dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
             }
           }
@@ -433,11 +456,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         }
     };
 
-    if (t_begin >= ntiles) continue;  // no query row sees these keys (uniform)
+    if (t_lo >= ntiles) continue;  // none of this head's tiles in the run (uniform)
     __syncthreads();  // the previous head's last tile is no longer read
-    load(t_begin, q_buf0, w_buf0, r_buf0);
+    load(t_lo, q_buf0, w_buf0, r_buf0);
     __syncthreads();
-    for (int t = t_begin; t < ntiles; t += 2) {
+    for (int t = t_lo; t < ntiles; t += 2) {
       if (t + 1 < ntiles) load(t + 1, q_buf1, w_buf1, r_buf1);
       if (!CAUSAL || t * BQ + BQ - 1 + off >= wk0) compute_tile(q_buf0, w_buf0, r_buf0, t * BQ);
       __syncthreads();
@@ -449,8 +472,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   }
 
   if (!live) return;
-  float* ok = p.dk + kr * D;
-  float* ov = p.dv + kr * D;
+  // a split key tile writes its run's partial sums (zero for an empty run)
+  const size_t part_off = (size_t)sp * nbk * Tk * D;
+  float* ok = (p.n_split > 1 ? p.dk_part + part_off : p.dk) + kr * D;
+  float* ov = (p.n_split > 1 ? p.dv_part + part_off : p.dv) + kr * D;
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
@@ -462,6 +487,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         *(f32x4*)(ov + dm * 32 + 8 * i + 4 * half) =
             f32x4{dv[dm][4 * i], dv[dm][4 * i + 1], dv[dm][4 * i + 2], dv[dm][4 * i + 3]};
     }
+}
+
+// dk and dv of split key tiles: the sum of the n_split partial results, in split order.
+__global__ __launch_bounds__(256) void polar_bwd_split_sum_kernel(const BwdMfmaParams p) {
+  const long long n4 = p.part_n4;
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < 2 * n4; i += stride) {
+    const bool is_v = i >= n4;
+    const long long e = is_v ? i - n4 : i;
+    const f32x4* src = (const f32x4*)(is_v ? p.dv_part : p.dk_part) + e;
+    f32x4 acc = src[0];
+    for (int sp = 1; sp < p.n_split; ++sp) {
+      const f32x4 x = src[(size_t)sp * n4];
+      acc[0] += x[0];
+      acc[1] += x[1];
+      acc[2] += x[2];
+      acc[3] += x[3];
+    }
+    ((f32x4*)(is_v ? p.dv : p.dk))[e] = acc;
+  }
 }
 
 }  // namespace polar

@@ -3,6 +3,7 @@
 // never synchronises and keeps no mutable global state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -415,18 +416,38 @@ polar_status merge_with_lens(const polar_problem* pr, const float* partials, int
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kBwdWaves = 4;  // matrix-core backward: 32 rows (or keys) per wave
+
+// Workgroups per key tile of the matrix-core dk/dv kernels.  One workgroup per (key tile,
+// kv head) gives B * Hkv * Tk / 128 workgroups, which for a long single sequence is about
+// one per resident slot (256 CUs x 2); under a causal mask the first key tile has ~Tq/128
+// times the work of the last, so the launch would last as long as its heaviest workgroup.
+// Each key tile's (head, query tile) pairs are then cut into n contiguous runs, enough for
+// four workgroups per slot (causal) or one (full mask), at most 4 per query head.
+int bwd_splits(const polar_problem* pr) {
+  if (pr->seq_q == 0) return 1;
+  const long long base = (long long)pr->batch * pr->kv_heads * ((pr->seq_k + kBwdWaves * 32 - 1) / (kBwdWaves * 32));
+  const long long target = pr->causal ? 2048 : 512;
+  const long long want = (target + base - 1) / base;
+  const long long cap = 4ll * (pr->heads / pr->kv_heads);
+  return (int)std::max(1ll, std::min(want, cap));
+}
+
 // Backward workspace.  fp32 inputs: w and the row constants in fp32, [rows, D + 4].
 // bf16 inputs: the forward's partial rows [rows, D + 3] fp32, then w as bf16 [rows, D],
-// then the row constants [rows] f32x4, each part starting on a 256-byte boundary.
+// then the row constants [rows] f32x4, then (split key tiles only) the partial dk and dv,
+// [splits, B, Hkv, Tk, D] fp32 each; every part starts on a 256-byte boundary.
 size_t bwd_workspace(const polar_problem* pr) {
   const size_t rows = (size_t)pr->batch * pr->heads * pr->seq_q;
   const size_t D = pr->head_dim;
   if (pr->dtype == POLAR_F32) return rows * (D + 4) * sizeof(float);
   if (rows == 0) return 0;
-  return align256(rows * (D + 3) * 4) + align256(rows * D * 2) + rows * 16;
+  const size_t base = align256(rows * (D + 3) * 4) + align256(rows * D * 2) + align256(rows * 16);
+  const int splits = bwd_splits(pr);
+  if (splits == 1) return base;
+  const size_t nk = (size_t)pr->batch * pr->kv_heads * pr->seq_k;
+  return base + 2 * align256((size_t)splits * nk * D * 4);
 }
-
-constexpr int kBwdWaves = 4;  // matrix-core backward: 32 rows (or keys) per wave
 
 // bf16 backward on the matrix cores: the forward in partial mode for the row statistics,
 // then the row constants, dq and dk/dv.
@@ -449,21 +470,25 @@ polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdM
   }
   // with no query rows this writes zero dk and dv
   mp.n_kt = (mp.Tk + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
-  const long long kblocks = (long long)mp.n_kt * mp.B * mp.Hkv;
+  const long long kblocks = (long long)mp.n_kt * mp.B * mp.Hkv * mp.n_split;
   if (kblocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
   // d = 64: dk and dv in one kernel with 32-row query tiles; d = 128: a dk kernel with
   // 32-row tiles and a dv kernel with 64-row tiles; all at 2 waves per SIMD
   const dim3 grid((unsigned)kblocks), block(kBwdWaves * 64);
   if constexpr (D == 64) {
-    return launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv>, grid, block, mp,
-                  stream);
+    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv>, grid, block, mp,
+                stream);
   } else {
     st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDk>, grid, block, mp,
                 stream);
     if (st != POLAR_OK) return st;
-    return launch(polar::polar_bwd_dkdv_mfma_kernel<D, 64, kBwdWaves, 2, CAUSAL, polar::kBwdDv>, grid, block, mp,
-                  stream);
+    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 64, kBwdWaves, 2, CAUSAL, polar::kBwdDv>, grid, block, mp,
+                stream);
   }
+  if (st != POLAR_OK || mp.n_split == 1) return st;
+  mp.part_n4 = (long long)mp.B * mp.Hkv * mp.Tk * D / 4;
+  const long long blocks = std::min((2 * mp.part_n4 + 255) / 256, 8192ll);
+  return launch(polar::polar_bwd_split_sum_kernel, dim3((unsigned)blocks), dim3(256), mp, stream);
 }
 
 template <int D, typename T, bool CAUSAL>
@@ -784,6 +809,12 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
     mp.g_count = g->d_count;
     mp.W = rows ? reinterpret_cast<__bf16*>(base + part_b) : nullptr;
     mp.R = rows ? reinterpret_cast<polar::f32x4*>(base + part_b + w_b) : nullptr;
+    mp.n_split = bwd_splits(pr);
+    if (mp.n_split > 1) {
+      const size_t split_b = align256((size_t)mp.n_split * nk * D * 4);
+      mp.dk_part = reinterpret_cast<float*>(base + part_b + w_b + align256(nq * 16));
+      mp.dv_part = reinterpret_cast<float*>(base + part_b + w_b + align256(nq * 16) + split_b);
+    }
     mp.dq = dq;
     mp.dk = dk;
     mp.dv = dv;

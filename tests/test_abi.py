@@ -301,9 +301,21 @@ def test_bwd_validation(lib):
     pr, keep = prob.to_c()
     rows = 2 * 4 * 48
     up = lambda x: (x + 255) // 256 * 256
-    # bf16: forward statistics (d + 3 fp32), w (d bf16), row constants (4 fp32), 256-byte parts
-    ws = up(rows * 131 * 4) + up(rows * 128 * 2) + rows * 16
+    # bf16: forward statistics (d + 3 fp32), w (d bf16), row constants (4 fp32), 256-byte
+    # parts; 4 key tiles (one per (b, kv head)) under a causal mask want 2048 / 4 runs each,
+    # clamped to 4 per query head (8): 8 partial dk and dv of 2 * 2 * 64 keys
+    nk = 2 * 2 * 64
+    ws = up(rows * 131 * 4) + up(rows * 128 * 2) + up(rows * 16) + 2 * up(8 * nk * 128 * 4)
     assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr)) == ws
+    # enough key tiles (16 * 8 * 16 = 2048): no split, no partial sums
+    big_pr, keep_big = good_problem(batch=16, heads=8, kv_heads=8, seq_q=2048, seq_k=2048, head_dim=128).to_c()
+    r_big = 16 * 8 * 2048
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(big_pr)) == (
+        up(r_big * 131 * 4) + up(r_big * 128 * 2) + up(r_big * 16))
+    # full mask: 512 / 4 = 128 runs wanted, clamped to 8
+    full_pr, keep_full = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128,
+                                      causal=False).to_c()
+    assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(full_pr)) == ws
     pr32, keep32 = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128,
                                 dtype=pa.POLAR_F32).to_c()
     assert lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr32)) == rows * (128 + 4) * 4

@@ -98,6 +98,29 @@ def test_bwd_tiny(Tq, Tk, causal):
     bwd_case(1, 2, 2, Tq, Tk, 64, torch.float32, causal, seed=540 + Tq + Tk, beta=[0.0, 1.0], kappa=[1.0, 2.0])
 
 
+def _split_free_workspace(B, H, Tq, d):
+    rows = B * H * Tq
+    up = lambda x: (x + 255) // 256 * 256
+    return up(rows * (d + 3) * 4) + up(rows * d * 2) + up(rows * 16)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,d,causal,runs", [
+    (1, 16, 16, 24, 4096, 64, False, 1),   # 16 * 32 = 512 key tiles, full mask: one run each
+    (4, 16, 16, 16, 4096, 128, True, 1),   # 4 * 16 * 32 = 2048 key tiles, causal: one run each
+    (1, 16, 8, 24, 4096, 128, False, 2),   # 256 key tiles, full mask: two runs each
+])
+def test_bwd_key_tile_runs(B, H, Hkv, Tq, Tk, d, causal, runs):
+    """dk and dv with the key side's work in one run per 128-key tile (written directly)
+    and in two runs (partial sums added by a second kernel); the workspace size says
+    which."""
+    prob = pa.Problem(batch=B, heads=H, kv_heads=Hkv, seq_q=Tq, seq_k=Tk, head_dim=d, causal=causal,
+                      dtype=pa.POLAR_BF16)
+    extra = 0 if runs == 1 else 2 * runs * B * Hkv * Tk * d * 4
+    assert pa.bwd_workspace_bytes(prob) == _split_free_workspace(B, H, Tq, d) + extra
+    bwd_case(B, H, Hkv, Tq, Tk, d, torch.bfloat16, causal, seed=570 + d + runs, tau=[0.05] * H,
+             beta=[0.5] * H)
+
+
 def test_bwd_explicit_softmax_scale_and_floor_off():
     bwd_case(1, 2, 1, 64, 96, 128, torch.bfloat16, True, seed=550, tau=[0.1, 0.3], scale=0.3)
 
