@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "bwd_dq_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dq_mfma_kernel"),
     "bwd_dk_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
     "bwd_dv_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
+    "bwd_split_sum_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_split_sum_kernel"),
 }
 
 
