@@ -47,8 +47,12 @@ struct GroupDecodeParams {
   HeadParams hp;
 };
 
+// Four query heads and no per-key floor: held to 128 registers (4 waves per SIMD), which
+// they fit without spills; the other instances keep the compiler's choice.
 template <int D, int G, int NW, int UNROLL, bool PAGED, int KF = POLAR_KEY_FLOOR_NULL>
-__global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const GroupDecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(G == 4 && KF == POLAR_KEY_FLOOR_NULL ? 4
+                                                                                                               : 1))) void
+polar_decode_group_kernel(const GroupDecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key (8 dims each)
   constexpr int KPW = 64 / LPK;       // keys per wave per step
   constexpr int NSLOT = NW * KPW;     // independent running states per query head
@@ -119,18 +123,32 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const Group
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   }
 
+  // paged: the block-table entries of an iteration's keys are loaded one iteration ahead,
+  // so the K/V loads never wait on a table read
+  int32_t next_blk[UNROLL];
+  auto table_entries = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int key = base + slot + u * NSLOT;
+      next_blk[u] = key < hi ? trow[key >> p.bs_log2] : 0;
+    }
+  };
+  if constexpr (PAGED) table_entries(lo);
+
   for (int base = lo; base < hi; base += NSLOT * UNROLL) {
     u32x4 kr[UNROLL], vr[UNROLL];
     bool ok[UNROLL];
+    int32_t blk[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) blk[u] = next_blk[u];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int key = base + slot + u * NSLOT;
       ok[u] = key < hi;
       size_t row = 0;
       if constexpr (PAGED) {
-        const int32_t blk = ok[u] ? trow[key >> p.bs_log2] : 0;
-        ok[u] = ok[u] && (uint32_t)blk < (uint32_t)p.num_blocks;
-        row = (((size_t)(uint32_t)blk << p.bs_log2) + (key & bs_mask)) * p.Hkv + hk;
+        ok[u] = ok[u] && (uint32_t)blk[u] < (uint32_t)p.num_blocks;
+        row = (((size_t)(uint32_t)blk[u] << p.bs_log2) + (key & bs_mask)) * p.Hkv + hk;
       } else {
         row = (size_t)key;
       }
@@ -143,6 +161,7 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_group_kernel(const Group
         vr[u] = u32x4{0, 0, 0, 0};
       }
     }
+    if constexpr (PAGED) table_entries(base + NSLOT * UNROLL);
     float vf[UNROLL][8];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)

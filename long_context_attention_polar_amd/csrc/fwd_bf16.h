@@ -41,10 +41,6 @@
 //     window and masks the tiles it starts in.
 #pragma once
 
-#ifndef POLAR_SCHED_HINTS
-#define POLAR_SCHED_HINTS 1
-#endif
-
 #include <type_traits>
 
 #include "polar_common.h"
