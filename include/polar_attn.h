@@ -175,7 +175,10 @@ typedef struct polar_outputs {
  * cores with an online softmax that also streams sum p^2 (rescaled by the square of
  * each correction factor).  Supports bf16 and fp32, head_dim 64 and 128, causal and
  * non-causal, seq_q <= seq_k when causal (rows aligned to the end of the keys).  Every
- * reading variant (a sliding window needs causal). */
+ * reading variant (a sliding window needs causal).  bf16: one head's K (and V) of
+ * seq_k * head_dim * 2 bytes plus 64 KiB must fit the 32-bit range of the kernel's buffer
+ * loads (seq_k <= 16,776,959 at head_dim 128, 33,553,919 at 64); beyond it
+ * POLAR_ERR_UNSUPPORTED. */
 polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const void* k,
                             const void* v, const polar_outputs* out, void* stream);
 
@@ -195,7 +198,7 @@ polar_status polar_attn_fwd(const polar_problem* problem, const void* q, const v
  * than `split` are not touched; a slot that never receives a piece must hold m = -inf.
  * Reading variants: all but a sliding window and POLAR_LEVEL_QNORM (the merge that
  * finishes the pieces has no queries); a per-key floor uses the floor of the row's count
- * in the whole context. */
+ * in the whole context.  The same bf16 size limit as polar_attn_fwd. */
 polar_status polar_attn_fwd_partial(const polar_problem* problem, const void* q, const void* k, const void* v,
                                     int32_t context_k, float* partials, int32_t num_splits, int32_t split,
                                     void* stream);
@@ -322,7 +325,8 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
  * workspace may overlap an input or another output.  batch == 0 enqueues nothing;
  * seq_q == 0 (q, dq and workspace may then be NULL) writes zero dk and dv.  The kernels
  * (three for fp32; four to six for bf16, the last summing split partial dk and dv in a
- * fixed order, so results are deterministic) run in order on `stream`. */
+ * fixed order, so results are deterministic) run in order on `stream`.  bf16: the size
+ * limit of polar_attn_fwd applies to seq_k and to seq_q (one head's Q). */
 polar_status polar_attn_bwd(const polar_problem* problem, const void* q, const void* k, const void* v,
                             const polar_grads* grads, float* dq, float* dk, float* dv, void* workspace,
                             size_t workspace_bytes, void* stream);

@@ -83,6 +83,13 @@ polar_status check_shape(const polar_problem* pr, bool& empty) {
   return POLAR_OK;
 }
 
+// The bf16 matrix-core kernels address one head's rows through a buffer resource whose
+// range and offsets are 32-bit: that head's bytes, plus a tile's worth of lane offsets,
+// must stay below 4 GiB.  (The fp32 and decode kernels index with 64-bit offsets.)
+bool bf16_head_fits(const polar_problem* pr, int64_t seq) {
+  return pr->dtype != POLAR_BF16 || (uint64_t)seq * (uint64_t)pr->head_dim * 2u + 65536u <= 0xFFFFFFFFull;
+}
+
 // Reading variant -> kernel constants, with the checks every entry point shares.
 polar_status variant_params(const polar_problem* pr, HeadParams& hp) {
   const polar_variant* v = pr->variant;
@@ -546,6 +553,7 @@ polar_status polar_attn_fwd(const polar_problem* pr, const void* q, const void* 
   if (st != POLAR_OK) return st;
   st = check_entry_variant(pr, fp.hp, Entry::kFwd, true);
   if (st != POLAR_OK) return st;
+  if (!bf16_head_fits(pr, pr->seq_k)) return POLAR_ERR_UNSUPPORTED;
   if (empty) return POLAR_OK;  // no rows: pointers of empty tensors may be NULL
   if (!q || !k || !v) return POLAR_ERR_NULL_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return POLAR_ERR_MISALIGNED;
@@ -711,6 +719,7 @@ polar_status polar_attn_fwd_partial(const polar_problem* pr, const void* q, cons
   if (st != POLAR_OK) return st;
   st = check_entry_variant(pr, fp.hp, Entry::kPartial, true);
   if (st != POLAR_OK) return st;
+  if (!bf16_head_fits(pr, pr->seq_k)) return POLAR_ERR_UNSUPPORTED;
   if (num_splits < 1 || split < 0 || split >= num_splits) return POLAR_ERR_BAD_SHAPE;
   if (context_k != 0) {
     if (context_k < pr->seq_q || context_k < 0) return POLAR_ERR_BAD_SHAPE;
@@ -764,6 +773,7 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   if (st != POLAR_OK) return st;
   st = check_entry_variant(pr, bp.hp, Entry::kBwd, true);
   if (st != POLAR_OK) return st;
+  if (!bf16_head_fits(pr, pr->seq_k) || !bf16_head_fits(pr, pr->seq_q)) return POLAR_ERR_UNSUPPORTED;
   if (!g) return POLAR_ERR_NULL_ARG;
   if (pr->batch == 0) return POLAR_OK;  // nothing to write
   // fp32 path: the grid's second dimension holds (batch, head) pairs

@@ -150,6 +150,25 @@ def test_fwd_rejects_bad_pointers(lib):
     assert call_fwd(lib, prob, out=outputs(count=fake(11))) == 7
 
 
+def test_bf16_head_size_limit(lib):
+    """bf16 kernels address one head's rows through 32-bit buffer loads: seq * head_dim * 2
+    bytes plus 64 KiB must fit; the fp32 kernels have no such limit.  Calls that pass the
+    check are stopped by an overlap of outputs, before any launch."""
+    overlap = outputs(count=fake(11))
+    for d, limit in ((128, 16_776_959), (64, 33_553_919)):
+        assert call_fwd(lib, good_problem(seq_k=limit + 1, head_dim=d)) == 3
+        assert call_fwd(lib, good_problem(seq_k=limit, head_dim=d), out=overlap) == 7
+        assert call_fwd(lib, good_problem(seq_k=limit + 1, head_dim=d, dtype=pa.POLAR_F32), out=overlap) == 7
+    pr, keep = good_problem(seq_k=16_776_960, head_dim=128).to_c()
+    assert lib.polar_attn_fwd_partial(ctypes.byref(pr), fake(1), fake(2), fake(3), 0, fake(12), 1, 0, None) == 3
+    # backward: the limit holds for the queries too
+    g = pa.PolarGrads(fake(20), fake(21), None, fake(22))
+    for kw in (dict(seq_q=64, seq_k=16_776_960), dict(seq_q=16_776_960, seq_k=64, causal=False)):
+        pr, keep = good_problem(head_dim=128, **kw).to_c()
+        assert lib.polar_attn_bwd(ctypes.byref(pr), fake(1), fake(2), fake(3), ctypes.byref(g), fake(4), fake(5),
+                                  fake(6), fake(7), 1 << 30, None) == 3
+
+
 def test_negative_tau_within_range_is_accepted_by_validation(lib):
     """1 + tau ln(seq_k) > 0 is the condition; tau = -0.1 at seq_k = 64 passes the check
     (the call is then stopped by an overlap of outputs, before any launch)."""
