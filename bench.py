@@ -13,7 +13,9 @@ already resident in HBM:
     beside the headline, not part of it);
   * backward (dq, dk, dv for upstream gradients of all four channels), bf16 inputs on the
     matrix cores, B=1, 16 query heads over 4 KV heads, T=16384, d=128, causal (reported
-    beside the headline, not part of it, and timed in a loop of its own after the steps).
+    beside the headline, not part of it, and timed in a loop of its own after the steps),
+    once self-contained and once given the row statistics of the forward
+    (polar_attn_bwd_saved), as a training step that keeps them runs it.
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -40,6 +42,7 @@ PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
 DECODE = "bf16_decode_b64_h8_tk65536_d128"
 PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
 BWD = "bf16_bwd_b1_h16_kv4_t16384_d128"
+BWD_SAVED = BWD + "_saved"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -236,6 +239,13 @@ def main():
     kwb = dict(causal=True, len_temp=wb.len_temp(), null_bias=wb.null_bias(), count_scale=wb.count_scale())
     parts.append(dict(name=BWD, w=wb, kind="backward", flops=backward_flops(wb), headline=False, separate=True,
                       run=lambda: pa.bwd(qb, kb, vb, grb, workspace=wsb, out=outb, **kwb)))
+    # the same backward given the row statistics a training forward keeps (the one-split
+    # partial forward); they are computed once, outside the timed calls
+    savedb = pa.fwd_partial(qb, kb, vb, **kwb)
+    wsbs = torch.empty(pa.bwd_saved_workspace_bytes(probb), dtype=torch.uint8, device=dev)
+    parts.append(dict(name=BWD_SAVED, w=wb, kind="backward", flops=backward_flops(wb), headline=False,
+                      separate=True,
+                      run=lambda: pa.bwd(qb, kb, vb, grb, workspace=wsbs, out=outb, saved=savedb, **kwb)))
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
@@ -326,6 +336,11 @@ def main():
                      "traffic_dk": measured_traffic("bwd_dk_b1_h16_kv4_t16384_d128"),
                      "note": "bf16 matrix-core path: forward statistics, row constants, dq, dk, dv; "
                              "10 d algorithmic flops per causal pair"},
+        "backward_saved": {"bound": "mfma", "achieved": res[BWD_SAVED]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": res[BWD_SAVED]["frac_bf16_peak"],
+                           "ms": res[BWD_SAVED]["ms_avg"],
+                           "note": "the same backward given the forward's saved row statistics "
+                                   "(polar_attn_bwd_saved): row constants, dq, dk, dv"},
         "parts": res,
         "source_digest": digest,
     }

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 5
+#define POLAR_ABI_VERSION 6
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -330,6 +330,23 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
 polar_status polar_attn_bwd(const polar_problem* problem, const void* q, const void* k, const void* v,
                             const polar_grads* grads, float* dq, float* dk, float* dv, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Backward from saved forward statistics: polar_attn_bwd for bf16 inputs without its
+ * forward pass.  A training step that runs its forward as polar_attn_fwd_partial
+ * (num_splits = 1, split = 0, context_k = 0, then polar_attn_merge for the channels) has
+ * every row's (m, S1, S2, acc) already; passing them as DEVICE `saved` [B, heads, seq_q,
+ * head_dim + 3] fp32 (16-byte aligned, that layout, computed for the same problem and
+ * inputs) skips the forward kernel the backward would otherwise run for them.  The
+ * results are then bitwise those of polar_attn_bwd.  Same arguments and rules as
+ * polar_attn_bwd otherwise; `saved` is an input (no output or the workspace may overlap
+ * it) and may be NULL when seq_q == 0.  fp32 inputs: POLAR_ERR_UNSUPPORTED (their
+ * vector-ALU backward forms its own row statistics).  The workspace, of
+ * polar_attn_bwd_saved_workspace_bytes bytes (0 for an invalid or fp32 problem), is that
+ * of polar_attn_bwd without the room for the statistics. */
+size_t polar_attn_bwd_saved_workspace_bytes(const polar_problem* problem);
+polar_status polar_attn_bwd_saved(const polar_problem* problem, const void* q, const void* k, const void* v,
+                                  const float* saved, const polar_grads* grads, float* dq, float* dk, float* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* polar_status_string(polar_status status);

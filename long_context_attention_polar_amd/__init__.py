@@ -135,6 +135,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_bwd.restype = ctypes.c_int
     lib.polar_attn_bwd_workspace_bytes.argtypes = [P]
     lib.polar_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.polar_attn_bwd_saved.argtypes = [P, vp, vp, vp, vp, Gr, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.polar_attn_bwd_saved.restype = ctypes.c_int
+    lib.polar_attn_bwd_saved_workspace_bytes.argtypes = [P]
+    lib.polar_attn_bwd_saved_workspace_bytes.restype = ctypes.c_size_t
     lib.polar_status_string.argtypes = [ctypes.c_int]
     lib.polar_status_string.restype = ctypes.c_char_p
     lib.polar_abi_version.argtypes = []
@@ -409,13 +413,20 @@ def bwd_workspace_bytes(prob: Problem) -> int:
     return int(load_library().polar_attn_bwd_workspace_bytes(ctypes.byref(pr)))
 
 
+def bwd_saved_workspace_bytes(prob: Problem) -> int:
+    pr, keep = prob.to_c()
+    return int(load_library().polar_attn_bwd_saved_workspace_bytes(ctypes.byref(pr)))
+
+
 def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_scale=None, softmax_scale=None,
-        workspace=None, out=None, variant=None):
+        workspace=None, out=None, variant=None, saved=None):
     """Backward of the forward (polar_attn_bwd): gradients of
     sum(grads["direction"] * direction) + sum(grads["n_eff"] * n_eff) + ... with respect to
     q, k, v.  grads maps any of "direction" [B,H,Tq,d], "n_eff", "confidence", "count"
     [B,H,Tq] to fp32 tensors on q's device (a missing entry is zero).  Returns a dict with
-    dq [B,H,Tq,d] and dk, dv [B,Hkv,Tk,d], fp32.  Work is enqueued on the current stream."""
+    dq [B,H,Tq,d] and dk, dv [B,Hkv,Tk,d], fp32.  Work is enqueued on the current stream.
+    saved: the forward's row statistics [B,H,Tq,d+3] (or [B,H,Tq,1,d+3]) fp32 as
+    fwd_partial writes them with one split; bf16 inputs only (polar_attn_bwd_saved)."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, dev)
@@ -436,7 +447,13 @@ def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_sca
             raise ValueError(f"grads[{name!r}] must be float32 {shape}")
         _check_tensor(f"grads[{name!r}]", t, dev)
     g = PolarGrads(*[_ptr(grads.get(name)) for name in GRAD_NAMES])
-    need = bwd_workspace_bytes(prob)
+    if saved is not None:
+        d = q.shape[-1]
+        if saved.dtype != torch.float32 or saved.numel() != prob.batch * prob.heads * prob.seq_q * (d + 3) or \
+                not saved.is_contiguous():
+            raise ValueError(f"saved must be contiguous float32 [B,H,Tq,{d + 3}]")
+        _check_tensor("saved", saved, dev)
+    need = bwd_saved_workspace_bytes(prob) if saved is not None else bwd_workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, dev)
@@ -449,9 +466,15 @@ def bwd(q, k, v, grads, *, causal=True, len_temp=None, null_bias=None, count_sca
             raise ValueError(f"out[{name!r}] must be float32 {tuple(like.shape)}")
         _check_tensor(f"out[{name!r}]", t, dev)
     pr, keep = prob.to_c()
-    _check(load_library().polar_attn_bwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g),
-                                         _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(dev)))
+    nbytes = workspace.numel() * workspace.element_size()
+    if saved is not None:
+        _check(load_library().polar_attn_bwd_saved(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(saved),
+                                                   ctypes.byref(g), _ptr(out["dq"]), _ptr(out["dk"]),
+                                                   _ptr(out["dv"]), _ptr(workspace), nbytes, _stream(dev)))
+    else:
+        _check(load_library().polar_attn_bwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g),
+                                             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
+                                             nbytes, _stream(dev)))
     return out
 
 
@@ -476,6 +499,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["PolarVariant", "VARIANT_CODES", "fwd", "bwd", "bwd_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["PolarVariant", "VARIANT_CODES", "fwd", "bwd", "bwd_workspace_bytes", "bwd_saved_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

@@ -441,29 +441,34 @@ int bwd_splits(const polar_problem* pr) {
 }
 
 // Backward workspace.  fp32 inputs: w and the row constants in fp32, [rows, D + 4].
-// bf16 inputs: the forward's partial rows [rows, D + 3] fp32, then w as bf16 [rows, D],
-// then the row constants [rows] f32x4, then (split key tiles only) the partial dk and dv,
-// [splits, B, Hkv, Tk, D] fp32 each; every part starts on a 256-byte boundary.
-size_t bwd_workspace(const polar_problem* pr) {
+// bf16 inputs: the forward's partial rows [rows, D + 3] fp32 (not when the caller passes
+// them in), then w as bf16 [rows, D], then the row constants [rows] f32x4, then (split
+// key tiles only) the partial dk and dv, [splits, B, Hkv, Tk, D] fp32 each; every part
+// starts on a 256-byte boundary.
+size_t bwd_workspace(const polar_problem* pr, bool saved = false) {
   const size_t rows = (size_t)pr->batch * pr->heads * pr->seq_q;
   const size_t D = pr->head_dim;
   if (pr->dtype == POLAR_F32) return rows * (D + 4) * sizeof(float);
   if (rows == 0) return 0;
-  const size_t base = align256(rows * (D + 3) * 4) + align256(rows * D * 2) + align256(rows * 16);
+  const size_t base =
+      (saved ? 0 : align256(rows * (D + 3) * 4)) + align256(rows * D * 2) + align256(rows * 16);
   const int splits = bwd_splits(pr);
   if (splits == 1) return base;
   const size_t nk = (size_t)pr->batch * pr->kv_heads * pr->seq_k;
   return base + 2 * align256((size_t)splits * nk * D * 4);
 }
 
-// bf16 backward on the matrix cores: the forward in partial mode for the row statistics,
-// then the row constants, dq and dk/dv.
+// bf16 backward on the matrix cores: the forward in partial mode for the row statistics
+// (unless the caller saved them), then the row constants, dq and dk/dv.
 template <int D, bool CAUSAL>
-polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdMfmaParams& mp, void* stream) {
+polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdMfmaParams& mp, bool run_fwd,
+                             void* stream) {
   polar_status st = POLAR_OK;
   if (mp.Tq > 0) {
-    st = launch_fwd<D, CAUSAL>(pr, fp, stream);
-    if (st != POLAR_OK) return st;
+    if (run_fwd) {
+      st = launch_fwd<D, CAUSAL>(pr, fp, stream);
+      if (st != POLAR_OK) return st;
+    }
     const long long rows = (long long)mp.B * mp.H * mp.Tq;
     if ((rows + 3) / 4 > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
     st = launch(polar::polar_bwd_prep_kernel<D, CAUSAL>, dim3((unsigned)((rows + 3) / 4)), dim3(256), mp, stream);
@@ -761,9 +766,17 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* pr) {
   return bwd_workspace(pr);
 }
 
-polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* k, const void* v,
-                            const polar_grads* g, float* dq, float* dk, float* dv, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+size_t polar_attn_bwd_saved_workspace_bytes(const polar_problem* pr) {
+  bool empty = false;
+  if (check_shape(pr, empty) != POLAR_OK || pr->dtype != POLAR_BF16) return 0;
+  return bwd_workspace(pr, true);
+}
+
+// Both backward entry points.  use_saved: the rows' forward statistics come from `saved`
+// ([rows, D + 3] fp32, bf16 inputs only) instead of a forward pass inside the call.
+static polar_status bwd_entry(const polar_problem* pr, const void* q, const void* k, const void* v,
+                              const float* saved, bool use_saved, const polar_grads* g, float* dq, float* dk,
+                              float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   bool empty = false;
   polar_status st = check_shape(pr, empty);
   if (st != POLAR_OK) return st;
@@ -774,17 +787,19 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   st = check_entry_variant(pr, bp.hp, Entry::kBwd, true);
   if (st != POLAR_OK) return st;
   if (!bf16_head_fits(pr, pr->seq_k) || !bf16_head_fits(pr, pr->seq_q)) return POLAR_ERR_UNSUPPORTED;
+  if (use_saved && pr->dtype != POLAR_BF16) return POLAR_ERR_UNSUPPORTED;
   if (!g) return POLAR_ERR_NULL_ARG;
   if (pr->batch == 0) return POLAR_OK;  // nothing to write
   // fp32 path: the grid's second dimension holds (batch, head) pairs
   if (pr->dtype == POLAR_F32 && (int64_t)pr->batch * pr->heads > 65535) return POLAR_ERR_UNSUPPORTED;
   const bool rows = pr->seq_q > 0;
-  const size_t ws = bwd_workspace(pr);
+  const size_t ws = bwd_workspace(pr, use_saved);
   if (!k || !v || !dk || !dv) return POLAR_ERR_NULL_ARG;
   if (rows && (!q || !dq)) return POLAR_ERR_NULL_ARG;
+  if (rows && use_saved && !saved) return POLAR_ERR_NULL_ARG;
   if (ws > 0 && !workspace) return POLAR_ERR_WORKSPACE;
   if (workspace_bytes < ws) return POLAR_ERR_WORKSPACE;
-  const void* a16[] = {q, k, v, dq, dk, dv, workspace, g->d_direction};
+  const void* a16[] = {q, k, v, dq, dk, dv, workspace, g->d_direction, saved};
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return POLAR_ERR_MISALIGNED;
   if (!aligned(g->d_n_eff, 4) || !aligned(g->d_confidence, 4) || !aligned(g->d_count, 4))
@@ -793,18 +808,19 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   const size_t nq = (size_t)pr->batch * pr->heads * pr->seq_q;
   const size_t nk = (size_t)pr->batch * pr->kv_heads * pr->seq_k;
   const size_t D = pr->head_dim;
-  const void* ins[7] = {q, k, v, g->d_direction, g->d_n_eff, g->d_confidence, g->d_count};
-  const size_t in_bytes[7] = {nq * D * eb, nk * D * eb, nk * D * eb, nq * D * 4, nq * 4, nq * 4, nq * 4};
+  const void* ins[8] = {q, k, v, g->d_direction, g->d_n_eff, g->d_confidence, g->d_count, saved};
+  const size_t in_bytes[8] = {nq * D * eb, nk * D * eb, nk * D * eb, nq * D * 4, nq * 4, nq * 4, nq * 4,
+                              nq * (D + 3) * 4};
   const void* outs[4] = {dq, dk, dv, workspace};
   const size_t out_bytes[4] = {nq * D * 4, nk * D * 4, nk * D * 4, ws};
   for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < 8; ++i)
       if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i])) return POLAR_ERR_ALIAS;
     for (int o2 = o + 1; o2 < 4; ++o2)
       if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return POLAR_ERR_ALIAS;
   }
   if (pr->dtype == POLAR_BF16) {
-    const size_t part_b = align256(nq * (D + 3) * 4);
+    const size_t part_b = use_saved ? 0 : align256(nq * (D + 3) * 4);
     const size_t w_b = align256(nq * D * 2);
     char* base = static_cast<char*>(workspace);
     polar::BwdMfmaParams mp;
@@ -812,7 +828,7 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
     mp.q = static_cast<const __bf16*>(q);
     mp.k = static_cast<const __bf16*>(k);
     mp.v = static_cast<const __bf16*>(v);
-    mp.part = rows ? reinterpret_cast<const float*>(base) : nullptr;
+    mp.part = !rows ? nullptr : use_saved ? saved : reinterpret_cast<const float*>(base);
     mp.g_dir = g->d_direction;
     mp.g_neff = g->d_n_eff;
     mp.g_conf = g->d_confidence;
@@ -855,10 +871,12 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
     fp.hp_stride = bp.hp_stride;
     fp.scale = bp.scale;
     fp.hp = bp.hp;
+    const bool run_fwd = !use_saved;
     if (pr->head_dim == 64)
-      return pr->causal ? launch_bwd_mfma<64, true>(pr, fp, mp, stream) : launch_bwd_mfma<64, false>(pr, fp, mp, stream);
-    return pr->causal ? launch_bwd_mfma<128, true>(pr, fp, mp, stream)
-                      : launch_bwd_mfma<128, false>(pr, fp, mp, stream);
+      return pr->causal ? launch_bwd_mfma<64, true>(pr, fp, mp, run_fwd, stream)
+                        : launch_bwd_mfma<64, false>(pr, fp, mp, run_fwd, stream);
+    return pr->causal ? launch_bwd_mfma<128, true>(pr, fp, mp, run_fwd, stream)
+                      : launch_bwd_mfma<128, false>(pr, fp, mp, run_fwd, stream);
   }
   bp.q = q;
   bp.k = k;
@@ -878,6 +896,18 @@ polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* 
   bp.Tq = pr->seq_q;
   bp.Tk = pr->seq_k;
   return dispatch_bwd<float>(pr, bp, stream);
+}
+
+polar_status polar_attn_bwd(const polar_problem* pr, const void* q, const void* k, const void* v,
+                            const polar_grads* g, float* dq, float* dk, float* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return bwd_entry(pr, q, k, v, nullptr, false, g, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+polar_status polar_attn_bwd_saved(const polar_problem* pr, const void* q, const void* k, const void* v,
+                                  const float* saved, const polar_grads* g, float* dq, float* dk, float* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(pr, q, k, v, saved, true, g, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

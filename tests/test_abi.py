@@ -150,6 +150,40 @@ def test_fwd_rejects_bad_pointers(lib):
     assert call_fwd(lib, prob, out=outputs(count=fake(11))) == 7
 
 
+def test_bwd_saved_validation(lib):
+    """polar_attn_bwd_saved: bf16 only; its workspace is polar_attn_bwd's without the
+    forward statistics; `saved` is a required, 16-byte aligned input that no output may
+    overlap (unless there are no query rows)."""
+    prob = good_problem(batch=2, heads=4, kv_heads=2, seq_q=48, seq_k=64, head_dim=128)
+    pr, keep = prob.to_c()
+    rows = 2 * 4 * 48
+    up = lambda x: (x + 255) // 256 * 256
+    full = lib.polar_attn_bwd_workspace_bytes(ctypes.byref(pr))
+    ws = lib.polar_attn_bwd_saved_workspace_bytes(ctypes.byref(pr))
+    assert ws == full - up(rows * 131 * 4)
+    pr32, keep32 = good_problem(dtype=pa.POLAR_F32).to_c()
+    assert lib.polar_attn_bwd_saved_workspace_bytes(ctypes.byref(pr32)) == 0
+    bad, keep2 = good_problem(head_dim=96).to_c()
+    assert lib.polar_attn_bwd_saved_workspace_bytes(ctypes.byref(bad)) == 0
+    g = pa.PolarGrads(fake(20), fake(21), None, fake(22))
+
+    def run(saved=8, q=1, dq=4, dk=5, work=7, nbytes=ws, problem=pr):
+        arg = lambda x: fake(x) if isinstance(x, int) else x
+        return lib.polar_attn_bwd_saved(ctypes.byref(problem), arg(q), fake(2), fake(3), arg(saved), ctypes.byref(g),
+                                        arg(dq), arg(dk), fake(6), arg(work), nbytes, None)
+
+    assert run(problem=pr32, nbytes=1 << 30) == 3
+    assert run(saved=None) == 1
+    assert run(saved=ctypes.c_void_p(FAKE + 8 * (1 << 34) + 8)) == 5
+    assert run(nbytes=ws - 1) == 6
+    assert run(dq=8) == 7                    # dq over saved
+    assert run(work=8) == 7                  # workspace over saved
+    # no query rows: saved, q, dq and the workspace may be NULL
+    rows0, keep5 = good_problem(seq_q=0, head_dim=128).to_c()
+    assert lib.polar_attn_bwd_saved_workspace_bytes(ctypes.byref(rows0)) == 0
+    assert run(problem=rows0, saved=None, q=None, dq=None, work=None, nbytes=0, dk=None) == 1   # dk is required
+
+
 def test_bf16_head_size_limit(lib):
     """bf16 kernels address one head's rows through 32-bit buffer loads: seq * head_dim * 2
     bytes plus 64 KiB must fit; the fp32 kernels have no such limit.  Calls that pass the

@@ -152,6 +152,57 @@ def test_bwd_rejects_bad_gradients():
         pa.bwd(q, q, q, {"logits": torch.zeros(1, 2, 8, device=DEV)})
 
 
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,d,causal", [
+    (1, 4, 4, 300, 300, 64, True), (2, 4, 2, 130, 130, 128, True), (1, 2, 1, 77, 200, 64, False),
+    (1, 4, 1, 1000, 1000, 128, True), (1, 2, 2, 1, 65, 128, True), (1, 2, 2, 64, 64, 64, False)])
+def test_bwd_saved_statistics_bitwise(B, H, Hkv, Tq, Tk, d, causal):
+    """polar_attn_bwd_saved fed the one-split partial forward gives exactly what
+    polar_attn_bwd gives: the same kernels run, only the forward pass inside the call is
+    replaced by the caller's statistics."""
+    print(f"[bwd] saved statistics B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} causal={causal}", flush=True)
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, Tq, Tk, d, torch.bfloat16, seed=Tq + d)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    gr = {n: t.to(DEV) for n, t in pin.random_grads(B, H, Tq, d, Tq + 3).items()}
+    kw = dict(causal=causal, len_temp=[0.05 * (h % 3) for h in range(H)], null_bias=[0.5 * h - 1.0 for h in range(H)],
+              count_scale=[1.0 + h for h in range(H)])
+    ref = pa.bwd(q, k, v, gr, **kw)
+    saved = pa.fwd_partial(q, k, v, **kw)
+    got = pa.bwd(q, k, v, gr, saved=saved, **kw)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(ref[key], got[key]), key
+
+
+def test_bwd_saved_statistics_no_rows_and_fp32():
+    k = torch.randn(1, 2, 50, 64, device=DEV).to(torch.bfloat16)
+    q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    saved = torch.empty(1, 2, 0, 67, device=DEV)
+    out = pa.bwd(q, k, k.clone(), {}, causal=False, saved=saved)
+    torch.cuda.synchronize()
+    assert torch.all(out["dk"] == 0) and torch.all(out["dv"] == 0)
+    q32 = torch.zeros(1, 2, 8, 64, device=DEV)
+    with pytest.raises(pa.PolarError):
+        pa.bwd(q32, q32, q32, {}, saved=torch.zeros(1, 2, 8, 67, device=DEV))
+    with pytest.raises(ValueError):
+        pa.bwd(q.new_zeros(1, 2, 8, 64), k, k, {}, causal=False, saved=torch.zeros(1, 2, 8, 66, device=DEV))
+
+
+def test_workload_backward_saved_16k():
+    """The benchmark's backward workload from saved statistics equals the self-contained
+    backward bitwise at full size."""
+    w = pin.WORKLOADS["bf16_bwd_b1_h16_kv4_t16384_d128"]
+    print("[bwd] saved statistics, workload", w.name, flush=True)
+    q, k, v, _ = pin.workload_inputs(w, DEV)
+    gr = {n: t.to(DEV) for n, t in pin.random_grads(w.B, w.H, w.Tq, w.d, w.extra["grad_seed"]).items()}
+    kw = dict(causal=True, len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+    ref = pa.bwd(q, k, v, gr, **kw)
+    saved = pa.fwd_partial(q, k, v, **kw)
+    got = pa.bwd(q, k, v, gr, saved=saved, **kw)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(ref[key], got[key]), key
+
+
 def test_workload_backward_16k():
     """The benchmark's backward workload at full size: dq of sampled rows against the
     oracle (row i alone over its visible keys gives the same dq_i), and two identities
