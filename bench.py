@@ -179,8 +179,8 @@ def main():
                     help="run one device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (prefill shards by head and "
-              "decode by KV range with the split merge; see the design notes). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (prefill would shard by head, "
+              "decode by KV range combined with the split merge). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

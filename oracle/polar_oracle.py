@@ -9,8 +9,9 @@ Attention and Gated-Delta Compression Memory" (gist.science, paper 2606.25156; t
 Spanish, Italian and French pages carry the same summary).  Citations below name a
 section of that summary as [ATMA §x].
 
-What is computed, per batch b, head h and query row i (reading R; every point the
-pages leave open is listed with its reading in the design notes of the repository):
+What is computed, per batch b, head h and query row i (reading R: where the pages
+leave a point open, the plainest form consistent with the rest is taken, as written
+here):
 
     V_i   = keys visible to query i: j <= i + (Tk - Tq) when causal, all Tk otherwise
     n_i   = |V_i|
