@@ -79,13 +79,71 @@ def test_fwd_scale_override_and_large_logits():
 def test_fwd_uniform_logits_exact_neff():
     """q = 0: every visible key has p = 1, so n_eff equals the visible count exactly."""
     T, d = 700, 128
+    g = torch.Generator(device=DEV).manual_seed(79)
     q = torch.zeros(1, 2, T, d, dtype=torch.bfloat16, device=DEV)
-    k = torch.randn(1, 2, T, d, device=DEV).to(torch.bfloat16)
-    v = torch.randn(1, 2, T, d, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, T, d, device=DEV, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 2, T, d, device=DEV, generator=g).to(torch.bfloat16)
     out = pa.fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
     n = torch.arange(1, T + 1, device=DEV, dtype=torch.float32)
     assert torch.equal(out["n_eff"][0, 0], n) and torch.equal(out["n_eff"][0, 1], n)
+
+
+def test_fwd_maximum_key_count_closed_forms():
+    """The longest key range the bf16 kernels address (one head's K and V at the top of the
+    32-bit range of their buffer loads: 16,776,959 keys at d = 128), checked against closed
+    forms of the definition, which the oracle cannot hold in memory at this size.
+      row 0, q = 0: every score is 0, so S1 = S2 = n, n_eff = n, u = normalize(sum_j v_j),
+        conf = n / (n + e^f) with f = sqrt(2 ln n).
+      row 1, q = a e_0, and the only key with a component along e_0 is the last one,
+        b e_0: its score is D = a b / sqrt(d), every other score is 0, so with m = D
+        S1 = 1 + (n - 1) e^-D, S2 = 1 + (n - 1) e^-2D, n_eff = S1^2 / S2,
+        u = normalize(v_last + e^-D sum_{j < last} v_j), conf = S1 / (S1 + e^(f - D)).
+    Together they show that every key up to the last one is read and counted."""
+    n, d, a, b = 16_776_959, 128, 16.0, 12.0
+    print(f"[parity] maximum key count n={n}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(80)
+    v = torch.randn(1, 1, n, d, device=DEV, generator=g).to(torch.bfloat16)
+    k = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=DEV)
+    k[0, 0, n - 1, 0] = b
+    q = torch.zeros(1, 1, 2, d, dtype=torch.bfloat16, device=DEV)
+    q[0, 0, 1, 0] = a
+    out = pa.fwd(q, k, v, causal=False, null_bias=[0.0], stats=True)
+    torch.cuda.synchronize()
+    # sum_j v_j in fp64 on the host, chunk by chunk
+    total = torch.zeros(d, dtype=torch.float64)
+    step = 1 << 20
+    for s in range(0, n, step):
+        total += v[0, 0, s:min(n, s + step)].cpu().double().sum(0)
+    v_last = v[0, 0, n - 1].cpu().double()
+    del k, v
+    torch.cuda.empty_cache()
+    D = a * b / math.sqrt(d)
+    f = math.sqrt(2.0 * math.log(n))
+    s1 = 1.0 + (n - 1) * math.exp(-D)
+    s2 = 1.0 + (n - 1) * math.exp(-2.0 * D)
+    acc1 = v_last + math.exp(-D) * (total - v_last)
+    want = {
+        "n_eff": [float(n), s1 * s1 / s2],
+        "confidence": [n / (n + math.exp(f)), s1 / (s1 + math.exp(f - D))],
+        "direction": [(total / total.norm()).numpy(), (acc1 / acc1.norm()).numpy()],
+        "m": [0.0, D], "s1": [float(n), s1], "s2": [float(n), s2],
+    }
+    want["count"] = [c * math.tanh(math.log(x)) for c, x in zip(want["confidence"], want["n_eff"])]
+    got = {key: to_np(t)[0, 0] for key, t in out.items() if torch.is_tensor(t)}
+    for i in range(2):
+        du = float(np.linalg.norm(got["direction"][i] - want["direction"][i]))
+        dn = abs(got["n_eff"][i] - want["n_eff"][i]) / want["n_eff"][i]
+        dc = abs(got["confidence"][i] - want["confidence"][i])
+        dk = abs(got["count"][i] - want["count"][i])
+        st = got["stats"][i]
+        print(f"[parity] max keys row {i}: direction {du:.2e} n_eff {dn:.2e} (gpu {got['n_eff'][i]:.6g}) "
+              f"confidence {dc:.2e} count {dk:.2e} stats {st}", flush=True)
+        assert du <= 2e-2 and dn <= 1e-2 and dc <= 1e-2 and dk <= 1e-2, i
+        assert abs(st[0] - want["m"][i]) <= 1e-3 * max(1.0, want["m"][i])
+        assert abs(st[1] - want["s1"][i]) <= 1e-2 * want["s1"][i] and abs(st[2] - want["s2"][i]) <= 1e-2 * want["s2"][i]
+    # q = 0: the weights are exactly 1 and their sums integers below 2^24
+    assert got["stats"][0][1] == n and got["stats"][0][2] == n
 
 
 def test_fwd_optional_outputs_and_determinism():
