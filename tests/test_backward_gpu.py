@@ -135,7 +135,7 @@ def test_bwd_constant_confidence_gives_zero():
 def test_bwd_no_query_rows():
     """seq_q == 0: dq is empty and dk, dv are written as zeros."""
     q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
-    k = torch.randn(1, 2, 50, 64, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, 50, 64, device=DEV, generator=torch.Generator(device=DEV).manual_seed(91)).to(torch.bfloat16)
     out = pa.bwd(q, k, k.clone(), {}, causal=False)
     torch.cuda.synchronize()
     assert out["dq"].numel() == 0
@@ -174,7 +174,7 @@ def test_bwd_saved_statistics_bitwise(B, H, Hkv, Tq, Tk, d, causal):
 
 
 def test_bwd_saved_statistics_no_rows_and_fp32():
-    k = torch.randn(1, 2, 50, 64, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, 50, 64, device=DEV, generator=torch.Generator(device=DEV).manual_seed(92)).to(torch.bfloat16)
     q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
     saved = torch.empty(1, 2, 0, 67, device=DEV)
     out = pa.bwd(q, k, k.clone(), {}, causal=False, saved=saved)
