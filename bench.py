@@ -15,7 +15,11 @@ already resident in HBM:
     matrix cores, B=1, 16 query heads over 4 KV heads, T=16384, d=128, causal (reported
     beside the headline, not part of it, and timed in a loop of its own after the steps),
     once self-contained and once given the row statistics of the forward
-    (polar_attn_bwd_saved), as a training step that keeps them runs it.
+    (polar_attn_bwd_saved), as a training step that keeps them runs it;
+  * beside the headline, also in loops of their own: the T=65536 prefill as a chunked
+    prefill (8 chunks of 8192 queries: partial forwards over the cached prefix and over
+    the chunk, merged), and under two reading variants (a per-key soft floor; a sliding
+    window of 4096 keys).
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -43,6 +47,11 @@ DECODE = "bf16_decode_b64_h8_tk65536_d128"
 PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
 BWD = "bf16_bwd_b1_h16_kv4_t16384_d128"
 BWD_SAVED = BWD + "_saved"
+CHUNK = 8192
+CHUNKED = f"bf16_chunked_prefill_b1_h16_t65536_d64_chunk{CHUNK}"
+SOFT_FLOOR = "bf16_b1_h16_t65536_d64_soft_key_floor"
+WIN = 4096
+WINDOW = f"bf16_b1_h16_t65536_d64_window{WIN}"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -102,6 +111,45 @@ def _code_lines(text):
 
 def prefill_flops(w):
     return 4 * w.d * w.pairs()
+
+
+def window_pairs(T, W):
+    """(query, key) pairs of a causal prefill whose rows see at most their last W keys."""
+    W = min(W, T)
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def chunked_prefill_plan(pa, torch, q, k, v, w, chunk, keep_outputs=False):
+    """A causal prefill in chunks of `chunk` queries, as a serving engine runs it: each
+    chunk's rows take a partial forward over the cached keys before the chunk (no mask)
+    and one over the chunk's own keys (causal), each with the length temperature of the
+    row's count in the whole context, and polar_attn_merge combines the two.  The cached
+    prefixes and the chunk slices are laid out once, outside the timed calls.  Returns the
+    callable that runs every chunk, writing each chunk's channels into one buffer, or with
+    keep_outputs also the list of (first row, outputs) of every chunk, each its own."""
+    B, H, T, d = q.shape
+    kw = dict(len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+    out = pa.allocate_outputs(B, H, chunk, d, q.device)
+    steps = []
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        S = 2 if c0 else 1
+        parts = torch.empty(B, H, c1 - c0, S, d + 3, dtype=torch.float32, device=q.device)
+        pre = (k[:, :, :c0].contiguous(), v[:, :, :c0].contiguous()) if c0 else None
+        own = keep_outputs or c1 - c0 != chunk
+        steps.append((c1, q[:, :, c0:c1].contiguous(), k[:, :, c0:c1].contiguous(), v[:, :, c0:c1].contiguous(),
+                      pre, S, parts, pa.allocate_outputs(B, H, c1 - c0, d, q.device) if own else out))
+
+    def run():
+        for c1, qc, kc, vc, pre, S, parts, o in steps:
+            if pre is not None:
+                pa.fwd_partial(qc, pre[0], pre[1], causal=False, context_k=c1, partials=parts, num_splits=S,
+                               split=0, **kw)
+            pa.fwd_partial(qc, kc, vc, causal=True, context_k=c1, partials=parts, num_splits=S, split=S - 1, **kw)
+            pa.merge(parts, seq_k=c1, causal=True, out=o, **kw)
+    if keep_outputs:
+        return run, [(c1 - len_q, o) for c1, qc, kc, vc, pre, S, parts, o in steps for len_q in [qc.shape[2]]]
+    return run
 
 
 def backward_flops(w):
@@ -202,13 +250,29 @@ def main():
         del a, b
 
     parts = []
+    resident = {}
     for name in PREFILL:
         w = pin.WORKLOADS[name]
         q, k, v, _ = pin.workload_inputs(w, dev)
+        resident[name] = (q, k, v)
         out = pa.allocate_outputs(w.B, w.H, w.Tq, w.d, dev)
         kw = dict(causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
         parts.append(dict(name=name, w=w, kind="prefill", flops=prefill_flops(w),
                           run=lambda q=q, k=k, v=v, out=out, kw=kw: pa.fwd(q, k, v, out=out, **kw)))
+    # beside the headline, each timed in a loop of its own after the steps: the T=65536
+    # prefill as a chunked prefill, and under two reading variants
+    wl = pin.WORKLOADS[PREFILL[1]]
+    ql, kl, vl = resident[PREFILL[1]]
+    chunked = chunked_prefill_plan(pa, torch, ql, kl, vl, wl, CHUNK)
+    parts.append(dict(name=CHUNKED, w=wl, kind="side", flops=prefill_flops(wl), headline=False, separate=True,
+                      run=chunked))
+    outl = pa.allocate_outputs(wl.B, wl.H, wl.Tq, wl.d, dev)
+    kwl = dict(causal=True, len_temp=wl.len_temp(), null_bias=wl.null_bias(), count_scale=wl.count_scale())
+    parts.append(dict(name=SOFT_FLOOR, w=wl, kind="side", flops=prefill_flops(wl), headline=False, separate=True,
+                      run=lambda: pa.fwd(ql, kl, vl, out=outl, variant={"key_floor": "soft"}, **kwl)))
+    parts.append(dict(name=WINDOW, w=wl, kind="side", flops=4 * wl.d * wl.B * wl.H * window_pairs(wl.Tq, WIN),
+                      headline=False, separate=True,
+                      run=lambda: pa.fwd(ql, kl, vl, out=outl, variant={"window": WIN}, **kwl)))
     wd = pin.WORKLOADS[DECODE]
     qd, kd, vd, _ = pin.workload_inputs(wd, dev)
     prob = pa.problem_for(qd, kd, causal=True, len_temp=wd.len_temp(), null_bias=wd.null_bias(),
@@ -293,7 +357,7 @@ def main():
             entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
             entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
             entry["flops_per_launch"] = p["flops"]
-        elif p["kind"] == "backward":
+        elif p["kind"] in ("backward", "side"):
             entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
             entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
             entry["flops_per_call"] = p["flops"]
@@ -336,6 +400,19 @@ def main():
                      "traffic_dk": measured_traffic("bwd_dk_b1_h16_kv4_t16384_d128"),
                      "note": "bf16 matrix-core path: forward statistics, row constants, dq, dk, dv; "
                              "10 d algorithmic flops per causal pair"},
+        "chunked_prefill": {"bound": "mfma", "achieved": res[CHUNKED]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": res[CHUNKED]["frac_bf16_peak"], "ms": res[CHUNKED]["ms_avg"],
+                            "note": f"the T=65536 d=64 prefill in {65536 // CHUNK} chunks of {CHUNK} queries: per "
+                                    "chunk a partial forward over the cached prefix and one over the chunk, then "
+                                    "the merge; the one-pass prefill's algorithmic flops"},
+        "variants": {
+            "soft_key_floor": {"bound": "mfma", "achieved": res[SOFT_FLOOR]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": res[SOFT_FLOOR]["frac_bf16_peak"],
+                               "ms": res[SOFT_FLOOR]["ms_avg"]},
+            f"window_{WIN}": {"bound": "mfma", "achieved": res[WINDOW]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": res[WINDOW]["frac_bf16_peak"], "ms": res[WINDOW]["ms_avg"],
+                              "note": "flops of the (query, key) pairs inside the window"},
+            "note": "the T=65536 d=64 prefill under reading variants: a per-key soft floor, and a sliding window"},
         "backward_saved": {"bound": "mfma", "achieved": res[BWD_SAVED]["tflops"], "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": res[BWD_SAVED]["frac_bf16_peak"],
                            "ms": res[BWD_SAVED]["ms_avg"],

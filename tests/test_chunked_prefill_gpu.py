@@ -10,7 +10,7 @@ import torch
 import long_context_attention_polar_amd as pa
 import polar_inputs as pin
 from oracle import polar_attention
-from tests.parity import assert_parity, to_np
+from tests.parity import TOL, assert_parity, errors, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +66,36 @@ def test_partial_writes_only_its_slot():
     torch.cuda.synchronize()
     assert torch.all(parts[:, :, :, 0] == 7.0) and torch.all(parts[:, :, :, 2] == 7.0)
     assert torch.isfinite(parts[:, :, :, 1]).all()
+
+
+def test_workload_chunked_prefill_t65536():
+    """The benchmark's chunked prefill of the T=65536 d=64 workload (8 chunks of 8192
+    queries, each over its cached prefix and itself, merged) at full size: sampled rows of
+    every chunk and head against the oracle within the bf16 tolerance, and every row
+    against the one-pass forward, which is itself within that tolerance of the oracle on
+    every row: two such results differ by at most twice the tolerance (their bf16 weights
+    are rounded against different reference maxima)."""
+    import bench
+    w = pin.WORKLOADS["bf16_b1_h16_t65536_d64_lentemp"]
+    print(f"[chunked] workload {w.name} in chunks of {bench.CHUNK}", flush=True)
+    q, k, v, _ = pin.workload_inputs(w, "cpu")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    run, outs = bench.chunked_prefill_plan(pa, torch, qd, kd, vd, w, bench.CHUNK, keep_outputs=True)
+    run()
+    kw = dict(len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+    full = pa.fwd(qd, kd, vd, causal=True, **kw)
+    torch.cuda.synchronize()
+    channels = ("direction", "n_eff", "confidence", "count")
+    r = np.random.default_rng(90)
+    qn, kn, vn = to_np(q), to_np(k), to_np(v)
+    for c0, o in outs:
+        c1 = c0 + o["n_eff"].shape[2]
+        e = errors({key: o[key] for key in channels}, {key: to_np(full[key][:, :, c0:c1]) for key in channels})
+        for key in channels:
+            assert e[key] <= 2 * TOL["bf16"][key], f"chunk [{c0}, {c1}) vs one pass {key}: {e}"
+        rows = np.unique(np.concatenate([[c0, c1 - 1], r.integers(c0, c1, 4)]))
+        ref = polar_attention(qn, kn, vn, causal=True, rows=rows, **kw)
+        sel = torch.as_tensor(rows - c0, device=DEV)
+        sub = {key: o[key][:, :, sel] for key in channels}
+        e2 = assert_parity(sub, {key: ref[key] for key in channels}, "bf16", label=f"chunk [{c0}, {c1}) vs oracle")
+        print(f"[chunked] rows [{c0}, {c1}): vs one pass {e}; sampled rows vs oracle {e2}", flush=True)
