@@ -41,10 +41,13 @@
  *              enqueues work; results are valid once the caller synchronises the stream.
  *   Memory     The library allocates nothing and keeps no mutable global state; calls
  *              on different streams may run concurrently.
- *   Errors     All argument checks run before the first HIP call; a call that returns
- *              anything but POLAR_OK has enqueued nothing.  POLAR_ERR_HIP reports a
- *              launch failure seen right after the launch; faults inside a kernel
- *              surface at the caller's next synchronisation.
+ *   Errors     All argument checks run before the first HIP call; a call rejected by
+ *              them (any status but POLAR_OK and POLAR_ERR_HIP) has enqueued nothing.
+ *              POLAR_ERR_HIP is the failure of a kernel launch as the launch itself
+ *              reports it (an error an unrelated HIP call left on the thread is neither
+ *              reported nor cleared); kernels the call launched before the failing one
+ *              stay enqueued.  Faults inside a kernel surface at the caller's next
+ *              synchronisation.
  *   Empty      batch == 0 or seq_q == 0 is valid and enqueues nothing; the data
  *              pointers of such a call may be NULL (polar_attn_bwd with seq_q == 0
  *              still writes zero dk and dv).

@@ -167,10 +167,14 @@ polar_status check_outputs(const polar_problem* pr, const polar_outputs* out, co
   return POLAR_OK;
 }
 
+// One launch; the status is the launch's own (hipLaunchKernel's result), so an error left
+// on the calling thread by an unrelated HIP call is neither reported nor cleared here.
 template <typename Kernel, typename Params>
 polar_status launch(Kernel kernel, dim3 grid, dim3 block, const Params& params, void* stream) {
-  hipLaunchKernelGGL(kernel, grid, block, 0, (hipStream_t)stream, params);
-  return hipGetLastError() == hipSuccess ? POLAR_OK : POLAR_ERR_HIP;
+  void* args[] = {const_cast<Params*>(&params)};
+  const hipError_t e =
+      hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? POLAR_OK : POLAR_ERR_HIP;
 }
 
 // Which entry point is checking a problem's reading variant.
