@@ -166,9 +166,10 @@ def decode_bytes(w):
     return kv + q + outs
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed PMC digest, or None when the kernel's
-    sources changed since the counters were taken."""
+def profiled(kernel_key, field):
+    """A figure of the committed rocprofv3 counter digest (HBM bytes per launch, MFMA busy
+    fraction, clock, ...), or None when the kernel's sources changed since the counters
+    were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
@@ -177,7 +178,12 @@ def measured_traffic(kernel_key):
     entry = data.get(kernel_key)
     if not entry or entry.get("source_digest") != source_digest(kernel_key):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get(field)
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed PMC digest (None when out of date)."""
+    return profiled(kernel_key, "hbm_bytes_per_launch")
 
 
 def cpu_baseline(seconds):
@@ -376,7 +382,15 @@ def main():
     big = res[PREFILL[1]]
     roofline = {"bound": "mfma", "achieved": big["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": big["tflops"] / PEAK_BF16_TFLOPS, "kernel": "polar_fwd_bf16_kernel<64,...> (T=65536 d=64)",
-                "traffic": measured_traffic("fwd_bf16_t65536_d64")}
+                "traffic": measured_traffic("fwd_bf16_t65536_d64"),
+                # from the committed counter profile of this kernel: matrix-core busy cycles
+                # over the dispatch's active cycles, and the clock it ran at
+                "mfma_busy": profiled("fwd_bf16_t65536_d64", "mfma_busy"),
+                "clock_ghz": profiled("fwd_bf16_t65536_d64", "clock_ghz")}
+    small = res[PREFILL[0]]
+    small.update({"mfma_busy": profiled("fwd_bf16_t16384_d128", "mfma_busy"),
+                  "clock_ghz": profiled("fwd_bf16_t16384_d128", "clock_ghz"),
+                  "traffic": measured_traffic("fwd_bf16_t16384_d128")})
     dec = res[DECODE]
     decode_roof = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": dec["frac_hbm_peak"], "ms": dec["ms_avg"],
