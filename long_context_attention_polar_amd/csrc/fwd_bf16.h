@@ -25,12 +25,13 @@
 //     V tile through two ds_read_b64_tr_b16 transpose reads, each delivering four
 //     consecutive keys of one dimension to a lane.
 //   * The weights of a tile are formed against the current reference maximum, with no
-//     maximum taken first.  When some lane's weights of the tile sum to more than 2^8 (so
-//     a weight may exceed 2^8; always on the wave's first tile), the wave moves the
+//     maximum taken first.  When some lane's weights of the tile sum to more than 2^16 (so
+//     a weight may exceed 2^16; always on the wave's first tile), the wave moves the
 //     reference of its rows to the tile maximum, rescales sum p and acc by alpha and
 //     sum p^2 by alpha^2, and forms the tile's weights again from its scores, which are
 //     still in registers.  Later moves happen only when a row's maximum grows by more
-//     than 2^8.  The variant that reports statistics tracks the true maximum on the side.
+//     than 16 in base-2 units.  The variant that reports statistics tracks the true
+//     maximum on the side.
 //   * sum p and sum p^2 are taken from the same bf16-rounded weights that enter P V, two
 //     at a time with v_dot2_f32_bf16 (exact products, fp32 sums), as per-lane partial
 //     sums combined once in the epilogue.
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) t_max[nb] = fmaxf(t_max[nb], lane_max(nb));
     }
-    // ---- a4: some weight of the wave may exceed 2^8 (a lane's tile sum does; always on
+    // ---- a4: some weight of the wave may exceed 2^16 (a lane's tile sum does; always on
     // the wave's first tile): move the reference of the rows to the tile maximum,
     // rescale sum p and acc by alpha and sum p^2 by alpha^2, and form the weights again
     bool big = false;

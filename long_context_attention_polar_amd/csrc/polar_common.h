@@ -28,9 +28,14 @@ constexpr float kMaxInit = -1.0e30f;
 // than this (base 2), so weights stay below 2^8 between moves.  The statistics are
 // exact for any reference; the true maximum is tracked on the side.
 constexpr float kRescaleSlack = 8.0f;
-// The same bound as a weight: the bf16 prefill kernel moves its reference when a lane's
-// weights of one tile sum to more than 2^8 (every weight is then at most 2^8).
-constexpr float kWeightLimit = 256.0f;
+// The bf16 prefill kernel moves its reference only when a lane's weights of one tile sum
+// to more than 2^16, so every weight stays at most 2^16 between moves.  bf16 weights and
+// fp32 sums round relative to their size, so the bound costs no precision, and with up to
+// 2^24 keys S1 <= 2^40, S1^2 <= 2^80 and S2 <= 2^56 stay far inside fp32.  A bound this
+// loose leaves the reference where the wave's first tile put it unless a row's maximum
+// grows by 16 (base 2) later, which a strongly tempered row's maximum otherwise does
+// often enough to make the rescale pass a measurable share of the loop.
+constexpr float kWeightLimit = 65536.0f;
 
 // Per-head parameters and the reading variant, copied by value into the kernel
 // arguments.
