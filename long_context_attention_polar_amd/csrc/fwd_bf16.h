@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           if constexpr (KF == POLAR_KEY_FLOOR_GATE) return t > fl ? fast_exp2(t) : 0.0f;
           return fast_exp2(t);
         };
-        float a1[2] = {0.0f, 0.0f}, a2[2] = {0.0f, 0.0f};
+        float a1 = 0.0f, a2 = 0.0f;  // one dot2 chain per sum
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -315,13 +315,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
               bf16x2 pp;
               pp[0] = (__bf16)weight(s[nb][mb][4 * i + j]);
               pp[1] = (__bf16)weight(s[nb][mb][4 * i + j + 1]);
-              a1[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, a1[j >> 1], false);
-              a2[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, a2[j >> 1], false);
+              a1 = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, a1, false);
+              a2 = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, a2, false);
               pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
               pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = pp[1];
             }
-        t1[nb] = a1[0] + a1[1];
-        t2[nb] = a2[0] + a2[1];
+        t1[nb] = a1;
+        t2[nb] = a2;
       }
     };
     auto lane_max = [&](int nb) __attribute__((always_inline)) {
