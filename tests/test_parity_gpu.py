@@ -146,6 +146,40 @@ def test_fwd_maximum_key_count_closed_forms():
     assert got["stats"][0][1] == n and got["stats"][0][2] == n
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_zero_values_give_zero_direction(dtype, d):
+    """acc = 0 (all values zero): the direction is the zero vector, exactly, on every path
+    (the norm is never divided by zero), and the other channels still match the oracle."""
+    print(f"[parity] zero values d={d} {dtype}", flush=True)
+    q, k, v, _ = pin.random_qkv(1, 2, 2, 200, 200, d, dtype, seed=60 + d)
+    v = torch.zeros_like(v)
+    kw = dict(len_temp=[0.0, 0.1], null_bias=[0.0, 1.0])
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=True, **kw)
+    assert not np.any(ref["direction"])
+    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["direction"]).item() == 0
+    assert_parity(out, ref, kind_of(dtype), label=f"zero values fwd d={d}")
+    if dtype == torch.bfloat16:
+        qd = q[:, :, -1:].contiguous()
+        ref_d = polar_attention(to_np(qd), to_np(k), to_np(v), causal=True, **kw)
+        for splits in (1, 3):
+            out_d = pa.decode(qd.to(DEV), k.to(DEV), v.to(DEV), num_splits=splits, **kw)
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(out_d["direction"]).item() == 0
+            assert_parity(out_d, ref_d, "bf16", label=f"zero values decode d={d} S={splits}")
+        # paged: blocks of 8 keys, in order
+        kp = k[0].permute(1, 0, 2).reshape(200 // 8, 8, 2, d).contiguous()
+        vp = torch.zeros_like(kp)
+        table = torch.arange(25, dtype=torch.int32).reshape(1, 25)
+        lens = torch.tensor([200], dtype=torch.int32)
+        out_p = pa.decode_paged(qd.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens.to(DEV), seq_k=200, **kw)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out_p["direction"]).item() == 0
+        assert_parity(out_p, ref_d, "bf16", label=f"zero values paged decode d={d}")
+
+
 def test_fwd_optional_outputs_and_determinism():
     q, k, v, _ = pin.random_qkv(1, 2, 2, 300, 300, 64, torch.bfloat16, 31)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
