@@ -67,6 +67,15 @@ def test_fwd_gqa_and_bottom_right_causal(dtype):
     run_case(1, 2, 2, 70, 333, 64, dtype, False, seed=13, beta=[0.0] * 2, label="Tq<Tk")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Tq,Tk", [(300, 70), (70, 300), (1, 129), (257, 1)])
+def test_fwd_noncausal_unequal_lengths(dtype, d, Tq, Tk):
+    """Without the mask every query sees all Tk keys, whatever Tq is."""
+    run_case(1, 4, 2, Tq, Tk, d, dtype, causal=False, seed=Tq * 7 + Tk + d, tau=[0.0, 0.1, 0.2, 0.05],
+             beta=[0.0, 0.5, -1.0, 2.0], label=f"noncausal Tq={Tq} Tk={Tk} d={d}")
+
+
 def test_fwd_scale_override_and_large_logits():
     q, k, v, _ = pin.random_qkv(1, 2, 2, 257, 257, 64, torch.bfloat16, 21)
     q = q * 4  # exact in bf16: large logits exercise the reference-maximum moves
