@@ -412,8 +412,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           }
         }
       // causal: key j is visible to row i iff j <= i + off; only tiles whose first rows
-      // precede the wave's last key need the mask
-      const bool masked = CAUSAL && i0 + off < wave_kmax;
+      // precede the wave's last key need the mask, applied in place in a pass of its own so
+      // that the other tiles carry no per-element compare
+      if (CAUSAL && i0 + off < wave_kmax) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (key > i0 + mb * 32 + 8 * i + 4 * half + j + off) s[mb][4 * i + j] = -INFINITY;
+      }
       bf16x8 pf[PS], dsf[PS];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -423,8 +432,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           for (int j = 0; j < 4; ++j) {
             const int r = mb * 32 + 8 * i + 4 * half + j;  // query row in the tile
             const f32x4 rv = rt[r];
-            float x = s[mb][4 * i + j];
-            if (masked && key > i0 + r + off) x = -INFINITY;
+            const float x = s[mb][4 * i + j];
             const float pv = fast_exp2(fmaf(rv[1], x, -rv[0]));
             if constexpr (DV) pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
             if constexpr (DK) {
