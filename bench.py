@@ -16,7 +16,8 @@ already resident in HBM:
     beside the headline, not part of it, and timed in a loop of its own after the steps),
     once self-contained and once given the row statistics of the forward
     (polar_attn_bwd_saved), as a training step that keeps them runs it;
-  * beside the headline, also in loops of their own: the T=65536 prefill as a chunked
+  * beside the headline, also in loops of their own: the B=4 H=8 T=4096 d=64 needle
+    prefill, the T=65536 prefill as a chunked
     prefill (8 chunks of 8192 queries: partial forwards over the cached prefix and over
     the chunk, merged), and under two reading variants (a per-key soft floor; a sliding
     window of 4096 keys).
@@ -51,6 +52,7 @@ CHUNK = 8192
 CHUNKED = f"bf16_chunked_prefill_b1_h16_t65536_d64_chunk{CHUNK}"
 SOFT_FLOOR = "bf16_b1_h16_t65536_d64_soft_key_floor"
 WIN = 4096
+NEEDLE = "bf16_b4_h8_t4096_d64_needle"
 WINDOW = f"bf16_b1_h16_t65536_d64_window{WIN}"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
@@ -276,6 +278,13 @@ def main():
     kwl = dict(causal=True, len_temp=wl.len_temp(), null_bias=wl.null_bias(), count_scale=wl.count_scale())
     parts.append(dict(name=SOFT_FLOOR, w=wl, kind="side", flops=prefill_flops(wl), headline=False, separate=True,
                       run=lambda: pa.fwd(ql, kl, vl, out=outl, variant={"key_floor": "soft"}, **kwl)))
+    # the needle workload (B=4, H=8, T=4096, d=64): throughput reported, no peak target
+    wn = pin.WORKLOADS[NEEDLE]
+    qn, kn, vn, _ = pin.workload_inputs(wn, dev)
+    outn = pa.allocate_outputs(wn.B, wn.H, wn.Tq, wn.d, dev)
+    kwn = dict(causal=True, len_temp=wn.len_temp(), null_bias=wn.null_bias(), count_scale=wn.count_scale())
+    parts.append(dict(name=NEEDLE, w=wn, kind="side", flops=prefill_flops(wn), headline=False, separate=True,
+                      run=lambda: pa.fwd(qn, kn, vn, out=outn, **kwn)))
     parts.append(dict(name=WINDOW, w=wl, kind="side", flops=4 * wl.d * wl.B * wl.H * window_pairs(wl.Tq, WIN),
                       headline=False, separate=True,
                       run=lambda: pa.fwd(ql, kl, vl, out=outl, variant={"window": WIN}, **kwl)))
@@ -419,6 +428,9 @@ def main():
                             "note": f"the T=65536 d=64 prefill in {65536 // CHUNK} chunks of {CHUNK} queries: per "
                                     "chunk a partial forward over the cached prefix and one over the chunk, then "
                                     "the merge; the one-pass prefill's algorithmic flops"},
+        "needle_prefill": {"bound": "mfma", "achieved": res[NEEDLE]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": res[NEEDLE]["frac_bf16_peak"], "ms": res[NEEDLE]["ms_avg"],
+                           "note": "bf16 B=4 H=8 T=4096 d=64 causal, one planted needle per head"},
         "variants": {
             "soft_key_floor": {"bound": "mfma", "achieved": res[SOFT_FLOOR]["tflops"], "peak": PEAK_BF16_TFLOPS,
                                "unit": "TFLOP/s", "frac": res[SOFT_FLOOR]["frac_bf16_peak"],

@@ -18,6 +18,7 @@ def test_prefill_flops_are_four_d_per_causal_pair():
         assert bench.prefill_flops(pin.WORKLOADS[name]) == 4 * d * H * T * (T + 1) // 2
     assert bench.prefill_flops(pin.WORKLOADS["bf16_b1_h16_t65536_d64_lentemp"]) == 8_796_227_239_936
     assert bench.prefill_flops(pin.WORKLOADS["bf16_b1_h16_t16384_d128_groups"]) == 1_099_578_736_640
+    assert bench.prefill_flops(pin.WORKLOADS[bench.NEEDLE]) == 68_736_253_952
 
 
 def test_backward_flops_are_ten_d_per_causal_pair():
