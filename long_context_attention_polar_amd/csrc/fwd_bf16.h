@@ -117,6 +117,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   constexpr int KS = D / 16;    // k-steps of Q K^T
   constexpr int DM = D / 32;    // 32-wide d blocks of P V
   constexpr int PS = BN / 16;   // k-steps of P V
+  // workgroups resident at once: 256 CUs x 4 SIMDs x OCC waves per SIMD, NW waves each
+  constexpr int kResidentBlocks = 256 * 4 * OCC / NW;
 
   __shared__ __attribute__((aligned(1024))) __bf16 k_buf0[BN * D];
   __shared__ __attribute__((aligned(1024))) __bf16 k_buf1[BN * D];
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   const int half = lane >> 5;
 
   int qt, bh;
-  tile_coords(blockIdx.x, p.n_qt, p.B * p.H, qt, bh);
+  tile_coords<kResidentBlocks>(blockIdx.x, p.n_qt, p.B * p.H, qt, bh);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int hk = h / (p.H / p.Hkv);

@@ -179,12 +179,19 @@ __device__ __forceinline__ void magnitude_channel(const HeadParams& hp, int hpi,
 // Block id -> (query tile, b*H + h).  Consecutive block ids are dispatched round-robin
 // over the 8 XCDs; when the head count allows it, every XCD receives whole heads so a
 // head's K/V tiles stay in one XCD's L2.  Within an XCD the heaviest (last, for causal)
-// query tiles are issued first.
+// query tiles are issued first.  RES > 0 is the number of workgroups the chip holds at
+// once; a grid that fits in one such round gives the second half of each XCD's blocks the
+// lightest tiles in reverse order, so that the two blocks the XCD places on one CU (its
+// k-th and its (c/2 + k)-th) sum to about the same causal work instead of the heavy end
+// setting the launch time.
+template <int RES = 0>
 __device__ __forceinline__ void tile_coords(int bid, int n_qt, int BH, int& qt, int& bh) {
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;
     const int xcd = bid & 7;
-    const int local = bid >> 3;
+    int local = bid >> 3;
+    const int c = n_qt * hpx;  // blocks per XCD
+    if (RES > 0 && c <= RES / 8 && (c & 1) == 0 && local >= c / 2) local = c - 1 - (local - c / 2);
     qt = n_qt - 1 - local / hpx;
     bh = xcd * hpx + local % hpx;
   } else {

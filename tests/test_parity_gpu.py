@@ -67,6 +67,18 @@ def test_fwd_gqa_and_bottom_right_causal(dtype):
     run_case(1, 2, 2, 70, 333, 64, dtype, False, seed=13, beta=[0.0] * 2, label="Tq<Tk")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,Hkv,T", [(1, 8, 8, 1000), (1, 8, 2, 700), (2, 8, 4, 520), (1, 16, 16, 300),
+                                       (1, 8, 8, 4096)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fwd_one_round_grids(d, B, H, Hkv, T, causal):
+    """Grids small enough to be resident at once, with heads in multiples of 8: the bf16
+    prefill then pairs each XCD's heavy and light query tiles (an even tile count per XCD)
+    or keeps the plain order (an odd one); every row of every tile against the oracle."""
+    run_case(B, H, Hkv, T, T, d, torch.bfloat16, causal, seed=T + 3 * d + H, beta=[0.0] * H,
+             label=f"one round B={B} H={H} T={T} d={d}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Tq,Tk", [(300, 70), (70, 300), (1, 129), (257, 1)])
