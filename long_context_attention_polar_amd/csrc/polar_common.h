@@ -181,9 +181,10 @@ __device__ __forceinline__ void magnitude_channel(const HeadParams& hp, int hpi,
 // head's K/V tiles stay in one XCD's L2.  Within an XCD the heaviest (last, for causal)
 // query tiles are issued first.  RES > 0 is the number of workgroups the chip holds at
 // once; a grid that fits in one such round gives the second half of each XCD's blocks the
-// lightest tiles in reverse order, so that the two blocks the XCD places on one CU (its
-// k-th and its (c/2 + k)-th) sum to about the same causal work instead of the heavy end
-// setting the launch time.
+// lightest tiles in reverse order.  An XCD that fills its CUs in the same order twice puts
+// its k-th and (c/2 + k)-th blocks on one CU, and these then sum to about the same causal
+// work, instead of the heavy tiles sharing CUs with the next-heaviest ones.  Only the
+// assignment of tiles to blocks changes, never a tile's arithmetic.
 template <int RES = 0>
 __device__ __forceinline__ void tile_coords(int bid, int n_qt, int BH, int& qt, int& bh) {
   if ((BH & 7) == 0) {
