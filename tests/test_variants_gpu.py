@@ -40,14 +40,15 @@ VARIANTS = {
 }
 
 
-def decidable_rows(q, k, causal, kw, variant):
-    """[B, H, Tq] mask: no visible score of the row within MARGIN of its floor (always
-    true without a per-key floor)."""
+def decidable_rows(q, k, causal, kw, variant, rows=None):
+    """[B, H, Tq] mask (or [B, H, len(rows)] for the given query rows): no visible score of
+    the row within MARGIN of its floor (always true without a per-key floor)."""
     var = variant_of(variant)
     q, k = to_np(q), to_np(k)
     B, H, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
-    ok = np.ones((B, H, Tq), dtype=bool)
+    rows = range(Tq) if rows is None else [int(i) for i in rows]
+    ok = np.ones((B, H, len(rows)), dtype=bool)
     if var["key_floor"] == "null":
         return ok
     scale = 1.0 / math.sqrt(d)
@@ -55,7 +56,7 @@ def decidable_rows(q, k, causal, kw, variant):
         for h in range(H):
             tau = kw["len_temp"][h] if kw.get("len_temp") else 0.0
             beta = kw["null_bias"][h]
-            for i in range(Tq):
+            for r, i in enumerate(rows):
                 hi = min(i + 1 + Tk - Tq, Tk) if causal else Tk
                 lo = max(0, hi - var["window"]) if var["window"] else 0
                 n = hi - lo
@@ -64,7 +65,7 @@ def decidable_rows(q, k, causal, kw, variant):
                 sigma = scale * float(np.sqrt(qi @ qi)) if var["floor_level"] == "qnorm" else 1.0
                 f = lam * sigma * floor_level(n, var) + beta
                 s = lam * scale * (k[b, h // (H // Hkv), lo:hi] @ qi)
-                ok[b, h, i] = np.min(np.abs(s - f)) > MARGIN
+                ok[b, h, r] = np.min(np.abs(s - f)) > MARGIN
     return ok
 
 
@@ -172,6 +173,28 @@ def test_prefill_window_sizes(window):
     out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, variant=variant, **kw)
     torch.cuda.synchronize()
     assert_parity(out, ref, "bf16", label=f"window {window}")
+
+
+@pytest.mark.parametrize("variant", [dict(key_floor="soft"), dict(window=4096)], ids=["soft_floor", "window4096"])
+def test_workload_variants_t65536(variant):
+    """The T=65536 d=64 workload (16 heads, per-head length temperatures) under the soft
+    per-key floor and under a 4096-key window, at full size and in the benchmark's launch
+    configuration (no statistics): sampled rows of every head against the variant oracle."""
+    w = pin.WORKLOADS["bf16_b1_h16_t65536_d64_lentemp"]
+    print(f"[variant] workload {w.name} {variant}", flush=True)
+    q, k, v, _ = pin.workload_inputs(w, "cpu")
+    kw = dict(len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, variant=variant, **kw)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(91)
+    # short rows (few visible keys, where the soft floor leaves keys above it), both sides of
+    # the window length, the last row and random ones
+    rows = np.unique(np.concatenate([[0, 1, 2, 3, 10, 31, 32, 63, 64, 100, 255, 256, 4095, 4096, 4097, w.Tq - 1],
+                                     r.integers(0, w.Tq, 8)]))
+    ref = polar_attention_variant(to_np(q), to_np(k), to_np(v), causal=True, variant=variant, rows=rows, **kw)
+    sel = torch.as_tensor(rows, device=DEV)
+    sub = {key: out[key][:, :, sel] for key in ("direction", "n_eff", "confidence", "count")}
+    compare(sub, ref, "bf16", decidable_rows(q, k, True, kw, variant, rows=rows), f"T=65536 {variant}")
 
 
 @pytest.mark.parametrize("name", sorted(VARIANTS))
