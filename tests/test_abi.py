@@ -320,7 +320,9 @@ def test_paged_decode_validation(lib):
 
 def test_grouped_auto_splits_count_group_chunks(lib):
     """A grouped workgroup serves up to 8 query heads of a group, so the automatic split
-    count is sized by (batch x kv_heads x chunks) workgroups."""
+    count is sized by (batch x kv_heads x chunks) workgroups; it aims for 4096 split
+    workgroups with one head per workgroup, 2048 with the grouped kernel over a contiguous
+    cache and 6144 over a paged pool."""
     mha = good_problem(batch=2, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
     gqa = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
     g3 = good_problem(batch=2, heads=6, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
@@ -329,8 +331,16 @@ def test_grouped_auto_splits_count_group_chunks(lib):
         pr, keep = prob.to_c()
         n[name] = lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0)
     assert n["mha"] == 4096 // 16          # 16 (b, h) rows
-    assert n["gqa"] == 4096 // 2 // 2 // 1  # 2 x 2 kv heads x 1 chunk of 4
-    assert n["g3"] == -(-4096 // (2 * 6))   # group of 3 runs one head per workgroup
+    assert n["gqa"] == 2048 // 2 // 2 // 1  # 2 x 2 kv heads x 1 chunk of 4
+    assert n["g3"] == -(-2048 // (2 * 6))   # group of 3 runs one head per workgroup
+    pr, keep = gqa.to_c()
+    kv = paged(num_blocks=1 << 17, max_blocks=1 << 16)
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == 6144 // 4
+    # at least 256 keys per split
+    short = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128)
+    pr, keep = short.to_c()
+    assert lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0) == 4
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(paged()), 0) == 4
 
 
 def test_fwd_partial_validation(lib):
