@@ -253,17 +253,21 @@ int group_chunk(const polar_problem* pr) {
   return 1;
 }
 
-// Split workgroups the automatic split count aims for, by kernel.  Measured: the
-// one-head-per-workgroup kernel ran the same from 2048 to 4096 workgroups; the grouped
-// kernel over a contiguous cache 1-3% faster at 2048 than at 4096, and over a shuffled
-// paged pool 5% faster at 6144 than at 4096 (more workgroups keep more of the scattered
-// block reads in flight).
+// Split workgroups the automatic split count aims for, by kernel, and the fewest keys a
+// split takes.  Measured: the one-head-per-workgroup kernel ran the same from 2048 to 4096
+// workgroups; the grouped kernel over a contiguous cache 1-3% faster at 2048 than at 4096;
+// over a shuffled paged pool 5% faster at 6144 than at 4096 (more workgroups keep more of
+// the scattered block reads in flight) while a split keeps at least 2048 keys, and 3%
+// slower at 6144 workgroups of 1365 keys than at 4096 of 2048.
 constexpr int kSplitTargetPlain = 4096;
 constexpr int kSplitTargetGrouped = 2048;
 constexpr int kSplitTargetPaged = 6144;
+constexpr int kSplitMinKeys = 256;
+constexpr int kSplitMinKeysPaged = 2048;
 
 int auto_splits(const polar_problem* pr, bool paged) {
-  // About the target's number of split workgroups, with at least 256 keys per split.  A
+  // About the target's number of split workgroups, with at least the minimum of keys per
+  // split (one split when the sequence is shorter).  A
   // workgroup serves one query head, or a chunk of a query-head group when heads share a
   // KV head.
   const long long rows = (long long)pr->batch * (pr->heads / group_chunk(pr));
@@ -271,7 +275,8 @@ int auto_splits(const polar_problem* pr, bool paged) {
   const long long target =
       paged ? kSplitTargetPaged : (pr->heads > pr->kv_heads ? kSplitTargetGrouped : kSplitTargetPlain);
   long long s = (target + rows - 1) / rows;
-  const long long max_by_len = (pr->seq_k + 255) / 256;
+  const long long min_keys = paged ? kSplitMinKeysPaged : kSplitMinKeys;
+  const long long max_by_len = (pr->seq_k + min_keys - 1) / min_keys;
   if (s > max_by_len) s = max_by_len;
   if (s < 1) s = 1;
   return (int)s;

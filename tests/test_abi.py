@@ -322,7 +322,7 @@ def test_grouped_auto_splits_count_group_chunks(lib):
     """A grouped workgroup serves up to 8 query heads of a group, so the automatic split
     count is sized by (batch x kv_heads x chunks) workgroups; it aims for 4096 split
     workgroups with one head per workgroup, 2048 with the grouped kernel over a contiguous
-    cache and 6144 over a paged pool."""
+    cache and 6144 over a paged pool, with splits of at least 256 keys (2048 paged)."""
     mha = good_problem(batch=2, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
     gqa = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
     g3 = good_problem(batch=2, heads=6, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
@@ -335,12 +335,17 @@ def test_grouped_auto_splits_count_group_chunks(lib):
     assert n["g3"] == -(-2048 // (2 * 6))   # group of 3 runs one head per workgroup
     pr, keep = gqa.to_c()
     kv = paged(num_blocks=1 << 17, max_blocks=1 << 16)
+    # paged: 6144 // 4 = 1536 splits wanted, but each keeps at least 2048 of the 2^20 keys
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == (1 << 20) // 2048
+    mid = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 23, causal=False, head_dim=128)
+    pr, keep = mid.to_c()
+    kv = paged(num_blocks=1 << 20, max_blocks=1 << 19)
     assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == 6144 // 4
-    # at least 256 keys per split
+    # at least 256 keys per split over a contiguous cache, 2048 over a paged pool
     short = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128)
     pr, keep = short.to_c()
     assert lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0) == 4
-    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(paged()), 0) == 4
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(paged()), 0) == 1
 
 
 def test_fwd_partial_validation(lib):

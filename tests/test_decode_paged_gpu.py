@@ -99,11 +99,13 @@ def test_paged_equals_contiguous_bitwise():
     kp, vp, table = make_paged(k, v, 16, 78)
     lens = torch.full((B,), Tk, dtype=torch.int32)
     for s in (1, 5, 0):
-        cont = pa.decode(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=s, null_bias=[0.0] * H, stats=True)
+        # 0: the paged call's automatic split count, which the contiguous call then uses
         pag = pa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens.to(DEV), seq_k=Tk,
                               num_splits=s, null_bias=[0.0] * H, stats=True)
+        cont = pa.decode(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=pag["splits"], null_bias=[0.0] * H,
+                         stats=True)
         torch.cuda.synchronize()
-        assert cont["splits"] == pag["splits"]
+        assert cont["splits"] == pag["splits"] and (s == 0 or pag["splits"] == s)
         assert torch.equal(cont["partials"], pag["partials"]), s
         for key in ("direction", "n_eff", "confidence", "count", "stats"):
             assert torch.equal(cont[key], pag[key]), (s, key)
