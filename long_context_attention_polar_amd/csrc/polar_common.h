@@ -105,6 +105,10 @@ struct MergeParams {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The per-row helpers below are compiled without floating-point contraction, so that
+// every kernel instantiation that inlines them (with or without statistics, prefill,
+// decode, merge) forms a row's temperature, floor and channels with the same roundings.
+
 // Keys visible to query row `row` (rows aligned to the end of the keys when causal).
 __device__ __forceinline__ int visible_keys(int row, int Tq, int Tk, bool causal) {
   int n = causal ? min(row + 1 + (Tk - Tq), Tk) : Tk;
@@ -122,6 +126,7 @@ __device__ __forceinline__ int context_count(int row, int Tq, int Tk, bool causa
 // Length temperature [ATMA §2.1, direction channel], by the form of the variant:
 // 1 + tau ln n (the default), tau ln n, or ln n / ln L.
 __device__ __forceinline__ float row_temperature(const HeadParams& hp, int hpi, int n) {
+#pragma clang fp contract(off)
   const float ln_n = logf((float)n);
   if (hp.lam_form == POLAR_TEMP_SSMAX) return hp.tau[hpi] * ln_n;
   if (hp.lam_form == POLAR_TEMP_TRAIN_RATIO) return ln_n * hp.inv_ln_train;
@@ -132,6 +137,7 @@ __device__ __forceinline__ float row_temperature(const HeadParams& hp, int hpi, 
 // then held at a tiny positive value, so masked scores stay -inf (never 0 * -inf) while
 // every visible exp2(c s - m) is exactly what c = 0 gives in fp32.
 __device__ __forceinline__ float logit_scale(float lam, float scale) {
+#pragma clang fp contract(off)
   return fmaxf(lam * scale * kLog2e, 1.0e-30f);
 }
 
@@ -140,6 +146,7 @@ __device__ __forceinline__ float logit_scale(float lam, float scale) {
 // b_n + gamma a_n with r = sqrt(2 ln n), b_n = r - (ln ln n + ln 4 pi) / (2 r), a_n = 1 / r.
 // One logit has mean 0.
 __device__ __forceinline__ float floor_level(const HeadParams& hp, int n) {
+#pragma clang fp contract(off)
   if (n <= 1) return 0.0f;
   const float ln_n = logf((float)n);
   const float r = sqrtf(2.0f * ln_n);
@@ -154,6 +161,7 @@ __device__ __forceinline__ float floor_level(const HeadParams& hp, int n) {
 // Null floor f = lam sigma l(n) + beta in tempered-logit units; sigma is 1, or
 // scale ||q|| for the data-adaptive level (the spread of the raw logits of the row).
 __device__ __forceinline__ float null_floor(const HeadParams& hp, int hpi, int n, float lam, float sigma) {
+#pragma clang fp contract(off)
   return lam * sigma * floor_level(hp, n) + hp.beta[hpi];
 }
 
@@ -166,6 +174,7 @@ __device__ __forceinline__ float null_floor(const HeadParams& hp, int hpi, int n
 __device__ __forceinline__ void magnitude_channel(const HeadParams& hp, int hpi, float m_nat, float S1, float S2,
                                                   float f, bool floor_on, float& neff, float& conf,
                                                   float& count) {
+#pragma clang fp contract(off)
   if (!(S1 > 0.0f)) {
     neff = conf = count = 0.0f;
     return;

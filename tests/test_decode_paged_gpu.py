@@ -91,13 +91,17 @@ def test_paged_group_sizes_and_block_sizes(group, block_size):
                beta=[0.0] * (2 * group))
 
 
-def test_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("Tk", [1000, 5500])
+def test_paged_equals_contiguous_bitwise(Tk):
     """The same grouped kernel over a shuffled pool and over the contiguous cache: only
-    row addresses differ, so the partials and the outputs are bitwise equal."""
-    B, H, Hkv, Tk, d = 2, 8, 2, 1000, 128
-    q, k, v, _ = pin.random_qkv(B, H, Hkv, 1, Tk, d, torch.bfloat16, 77)
+    row addresses differ, so the partials and the outputs are bitwise equal.  At 5500
+    keys the automatic split count of the paged call is above one (a split keeps at
+    least 2048 keys), so the automatic choice is exercised with several splits."""
+    B, H, Hkv, d = 2, 8, 2, 128
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, 1, Tk, d, torch.bfloat16, 77 + Tk)
     kp, vp, table = make_paged(k, v, 16, 78)
     lens = torch.full((B,), Tk, dtype=torch.int32)
+    ref = oracle_per_sequence(q, k, v, [Tk] * B, beta=[0.0] * H)
     for s in (1, 5, 0):
         # 0: the paged call's automatic split count, which the contiguous call then uses
         pag = pa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens.to(DEV), seq_k=Tk,
@@ -106,9 +110,12 @@ def test_paged_equals_contiguous_bitwise():
                          stats=True)
         torch.cuda.synchronize()
         assert cont["splits"] == pag["splits"] and (s == 0 or pag["splits"] == s)
+        if s == 0 and Tk > 4096:
+            assert pag["splits"] > 1, pag["splits"]
         assert torch.equal(cont["partials"], pag["partials"]), s
         for key in ("direction", "n_eff", "confidence", "count", "stats"):
             assert torch.equal(cont[key], pag[key]), (s, key)
+        assert_parity(pag, ref, "bf16", label=f"paged Tk={Tk} S={pag['splits']}")
 
 
 def test_grouped_matches_per_head_reads():
@@ -166,25 +173,31 @@ def test_paged_binding_rejects_bad_tensors():
 
 
 def test_workload_paged_decode_64k():
-    """The benchmark's paged GQA decode at full size, checked on sampled (b, h) rows: the
-    oracle reads sequence b's keys back out of the pool in logical order."""
+    """The benchmark's paged GQA decode at full size, every (sequence, query head) row
+    against the oracle: for each (sequence, KV head) the oracle reads that sequence's keys
+    back out of the pool in logical order and computes all query heads of the group."""
     w = pin.WORKLOADS["bf16_paged_decode_b64_h32_kv8_tk65536_d128"]
     print("[parity] paged decode workload", flush=True)
     q, kp, vp, table, lens = pin.paged_decode_inputs(w, DEV)
     out = pa.decode_paged(q, kp, vp, table, lens, seq_k=w.Tk, len_temp=w.len_temp(), null_bias=w.null_bias(),
                           count_scale=w.count_scale(), stats=True)
     torch.cuda.synchronize()
+    assert out["splits"] > 1
     group = w.H // w.Hkv
-    r = np.random.default_rng(71)
-    for b, h in [(0, 0), (63, 31)] + [tuple(x) for x in zip(r.integers(0, 64, 3), r.integers(0, 32, 3))]:
-        hk = h // group
-        kb = kp[table[b].long(), :, hk].reshape(1, 1, w.Tk, w.d)
-        vb = vp[table[b].long(), :, hk].reshape(1, 1, w.Tk, w.d)
-        ref = polar_attention(to_np(q[b:b + 1, h:h + 1]), to_np(kb), to_np(vb), causal=False,
-                              len_temp=[w.len_temp()[h]], null_bias=[w.null_bias()[h]],
-                              count_scale=[w.count_scale()[h]])
-        sub = {key: (t[b:b + 1, h:h + 1] if torch.is_tensor(t) else t) for key, t in out.items()
-               if key not in ("partials", "splits")}
-        assert_parity(sub, ref, "bf16", label=f"paged decode b={b} h={h}")
+    worst = {}
+    for b in range(w.B):
+        rows = table[b].long()
+        for hk in range(w.Hkv):
+            heads = slice(hk * group, (hk + 1) * group)
+            kb = kp[rows, :, hk].reshape(1, 1, w.Tk, w.d)
+            vb = vp[rows, :, hk].reshape(1, 1, w.Tk, w.d)
+            ref = polar_attention(to_np(q[b:b + 1, heads]), to_np(kb), to_np(vb), causal=False,
+                                  len_temp=w.len_temp()[heads], null_bias=w.null_bias()[heads],
+                                  count_scale=w.count_scale()[heads])
+            sub = {key: (t[b:b + 1, heads] if torch.is_tensor(t) else t) for key, t in out.items()
+                   if key not in ("partials", "splits")}
+            e = assert_parity(sub, ref, "bf16", label=f"paged decode b={b} hk={hk}")
+            worst = {n: max(worst.get(n, 0.0), x) for n, x in e.items()}
+    print(f"[parity] paged decode max errors over all {w.B * w.H} rows {worst}", flush=True)
     del kp, vp
     torch.cuda.empty_cache()

@@ -201,6 +201,26 @@ def test_zero_values_give_zero_direction(dtype, d):
         assert_parity(out_p, ref_d, "bf16", label=f"zero values paged decode d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,causal", [(1, 2, 2, 300, 300, True), (2, 4, 2, 1000, 1000, True),
+                                                  (1, 4, 1, 70, 333, True), (1, 2, 2, 257, 129, False),
+                                                  (1, 8, 8, 4097, 4097, True)])
+def test_fwd_statistics_off_bitwise(d, B, H, Hkv, Tq, Tk, causal):
+    """The instantiation without statistics (the one the benchmark times) and the one
+    with them compute the same channels bitwise: tracking the true row maximum on the
+    side changes no weight, sum or accumulator.  The statistics-on outputs are checked
+    against the oracle here as well."""
+    print(f"[parity] statistics off d={d} B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} causal={causal}", flush=True)
+    q, k, v, _ = pin.random_qkv(B, H, Hkv, Tq, Tk, d, torch.bfloat16, seed=Tq + Tk + d + H)
+    kw = dict(causal=causal, len_temp=[0.02 * h for h in range(H)], null_bias=[0.0] * H)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    on = pa.fwd(qd, kd, vd, stats=True, **kw)
+    off = pa.fwd(qd, kd, vd, out=pa.allocate_outputs(B, H, Tq, d, DEV), **kw)
+    torch.cuda.synchronize()
+    assert_same_channels(on, off, "statistics off")
+    assert_parity(on, polar_attention(to_np(q), to_np(k), to_np(v), **kw), "bf16", label=f"statistics on d={d}")
+
+
 def test_fwd_optional_outputs_and_determinism():
     q, k, v, _ = pin.random_qkv(1, 2, 2, 300, 300, 64, torch.bfloat16, 31)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -302,13 +322,35 @@ def test_merge_entry_point_on_oracle_partials():
 
 # ---------------------------------------------------------------- the named workloads
 
+CHANNELS = ("direction", "n_eff", "confidence", "count")
+
+
+def bench_call(q, k, v, w):
+    """The prefill call the benchmark times: statistics off (the kernel instantiation
+    that does not track the true row maximum), outputs from allocate_outputs."""
+    out = pa.allocate_outputs(w.B, w.H, w.Tq, w.d, q.device)
+    return pa.fwd(q, k, v, out=out, causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(),
+                  count_scale=w.count_scale())
+
+
+def assert_same_channels(a, b, label):
+    """Bitwise equality of the four channels of two forward calls."""
+    for key in CHANNELS:
+        assert torch.equal(a[key], b[key]), f"{label}: {key} differs"
+
+
 def workload_case(name):
+    """A named workload: every row against the oracle (statistics on), and the
+    benchmark's own call (statistics off) bitwise equal to it on every channel."""
     w = pin.WORKLOADS[name]
     print(f"[parity] {name}", flush=True)
     q, k, v, meta = pin.workload_inputs(w, "cpu")
-    out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(),
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = pa.fwd(qd, kd, vd, causal=w.causal, len_temp=w.len_temp(), null_bias=w.null_bias(),
                  count_scale=w.count_scale(), stats=True)
+    timed = bench_call(qd, kd, vd, w)
     torch.cuda.synchronize()
+    assert_same_channels(out, timed, f"{name} benchmark call")
     ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=w.causal, len_temp=w.len_temp(),
                           null_bias=w.null_bias(), count_scale=w.count_scale())
     e = assert_parity(out, ref, kind_of(w.dtype), label=name)
@@ -341,13 +383,24 @@ def lentemp_run():
     if not _LENTEMP:
         w = pin.WORKLOADS["bf16_b1_h16_t65536_d64_lentemp"]
         q, k, v, _ = pin.workload_inputs(w, "cpu")
-        out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, len_temp=w.len_temp(),
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        out = pa.fwd(qd, kd, vd, causal=w.causal, len_temp=w.len_temp(),
                      null_bias=w.null_bias(), count_scale=w.count_scale(), stats=True)
+        timed = bench_call(qd, kd, vd, w)
         torch.cuda.synchronize()
-        _LENTEMP.update(w=w, q=q, k=k, v=v, out={n: t.cpu() for n, t in out.items() if torch.is_tensor(t)})
-        del out
+        same = {key: torch.equal(out[key], timed[key]) for key in CHANNELS}
+        _LENTEMP.update(w=w, q=q, k=k, v=v, out={n: t.cpu() for n, t in out.items() if torch.is_tensor(t)},
+                        bench_same=same)
+        del out, timed, qd, kd, vd
         torch.cuda.empty_cache()
     return _LENTEMP
+
+
+def test_workload_lentemp_bench_call_bitwise():
+    """The T=65536 prefill as the benchmark times it (statistics off) gives bitwise the
+    channels of the statistics-on call that the per-head tests check on every row."""
+    r = lentemp_run()
+    assert all(r["bench_same"].values()), r["bench_same"]
 
 
 @pytest.mark.parametrize("h", range(16))
