@@ -39,8 +39,10 @@
  *              Outputs must not overlap the inputs.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *              enqueues work; results are valid once the caller synchronises the stream.
- *   Memory     The library allocates nothing and keeps no mutable global state; calls
- *              on different streams may run concurrently.
+ *   Memory     The library allocates nothing.  Its only mutable global state is the
+ *              per-device address of the array polar_attn_decode_noalloc uses, set
+ *              once per device on first use.  Calls on different streams may run
+ *              concurrently, except polar_attn_decode_noalloc calls on one GPU.
  *   Errors     All argument checks run before the first HIP call; a call rejected by
  *              them (any status but POLAR_OK and POLAR_ERR_HIP) has enqueued nothing.
  *              POLAR_ERR_HIP is the failure of a kernel launch as the launch itself
@@ -62,7 +64,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 6
+#define POLAR_ABI_VERSION 7
 /* Per-head parameter tables (len_temp, null_bias, count_scale) are supported up to
  * this many heads; with all three tables NULL any head count is accepted. */
 #define POLAR_MAX_PARAM_HEADS 128
@@ -226,6 +228,28 @@ size_t polar_attn_decode_workspace_bytes(const polar_problem* problem, int32_t n
 polar_status polar_attn_decode(const polar_problem* problem, const void* q, const void* k_cache,
                                const void* v_cache, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, const polar_outputs* out, void* stream);
+
+/* Size of the device array the no-allocation decode keeps its split partials in: one
+ * array per GPU, held from the first call on that GPU until the process ends. */
+#define POLAR_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* Split-KV decode that allocates nothing, for callers that cannot call hipMalloc or
+ * take a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same problem rules, arguments, kernels and results as
+ * polar_attn_decode (bitwise equal for the same num_splits), but the per-split partials
+ * go to a library-owned device array of POLAR_NOALLOC_SCRATCH_BYTES bytes on the GPU
+ * that `stream` belongs to (the current device for the NULL stream), instead of a
+ * caller workspace.  Partials above that size ([B, heads, S, head_dim + 3] fp32 for the
+ * split count S the call uses) are rejected with POLAR_ERR_WORKSPACE before any HIP
+ * call.  The first call on a GPU looks up the array's device address (briefly making
+ * that GPU current if it is not); a failure of that lookup is POLAR_ERR_HIP.  Every
+ * call on one GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (concurrent streams, or host threads) race and must be
+ * serialised by the caller.  No call needs the array cleared: every partial row is
+ * written before it is read. */
+polar_status polar_attn_decode_noalloc(const polar_problem* problem, const void* q, const void* k_cache,
+                                       const void* v_cache, int32_t num_splits, const polar_outputs* out,
+                                       void* stream);
 
 /* Paged KV cache for polar_attn_decode_paged.  The keys of sequence b are stored in
  * blocks of block_size rows: block_table[b * max_blocks + j] is the pool block holding

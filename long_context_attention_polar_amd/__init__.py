@@ -7,6 +7,7 @@ mirror the C ABI in include/polar_attn.h:
     fwd(q, k, v, ...)            -> polar_attn_fwd      (fused prefill forward)
     bwd(q, k, v, grads, ...)     -> polar_attn_bwd      (dq, dk, dv of the forward)
     decode(q, k_cache, v_cache)  -> polar_attn_decode   (split-KV decode + merge)
+    decode_noalloc(...)          -> polar_attn_decode_noalloc (the same, no workspace)
     merge(partials, ...)         -> polar_attn_merge    (merge of split statistics)
     decode_num_splits / decode_workspace_bytes / status_string / abi_version
 
@@ -119,6 +120,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_merge.restype = ctypes.c_int
     lib.polar_attn_decode_num_splits.argtypes = [P, ctypes.c_int32]
     lib.polar_attn_decode_num_splits.restype = ctypes.c_int32
+    lib.polar_attn_decode_noalloc.argtypes = [P, vp, vp, vp, ctypes.c_int32, O, vp]
+    lib.polar_attn_decode_noalloc.restype = ctypes.c_int
     lib.polar_attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.polar_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.polar_attn_fwd_partial.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp]
@@ -339,6 +342,26 @@ def decode(q, k_cache, v_cache, *, num_splits=0, len_temp=None, null_bias=None, 
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 8 << 20  # POLAR_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, k_cache, v_cache, out, *, num_splits=0, len_temp=None, null_bias=None, count_scale=None,
+                   softmax_scale=None, variant=None):
+    """Split-KV decode that allocates nothing (polar_attn_decode_noalloc): as decode(),
+    but the split partials live in the library's own per-GPU array, so the caller passes
+    the outputs (see allocate_outputs) and no workspace.  Returns `out`."""
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(name, t, dev)
+    prob = problem_for(q, k_cache, causal=True, len_temp=len_temp, null_bias=null_bias,
+                       count_scale=count_scale, softmax_scale=softmax_scale, variant=variant)
+    pr, keep = prob.to_c()
+    oc = _outputs_c(out)
+    _check(load_library().polar_attn_decode_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                    num_splits, ctypes.byref(oc), _stream(dev)))
+    return out
+
+
 def _partials_view(workspace, prob, splits):
     n = prob.batch * prob.heads * prob.seq_q * splits * (prob.head_dim + 3)
     return workspace[:n * 4].view(torch.float32).view(prob.batch, prob.heads, prob.seq_q, splits, prob.head_dim + 3)
@@ -499,6 +522,6 @@ def merge(partials, *, seq_k, causal=True, len_temp=None, null_bias=None, count_
     return out
 
 
-__all__ = ["PolarVariant", "VARIANT_CODES", "fwd", "bwd", "bwd_workspace_bytes", "bwd_saved_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
+__all__ = ["PolarVariant", "VARIANT_CODES", "fwd", "bwd", "decode_noalloc", "NOALLOC_SCRATCH_BYTES", "bwd_workspace_bytes", "bwd_saved_workspace_bytes", "PolarGrads", "fwd_partial", "decode", "decode_paged", "paged_kv", "decode_paged_workspace_bytes", "merge", "decode_num_splits", "decode_workspace_bytes", "abi_version",
            "status_string", "load_library", "Problem", "PolarError", "PolarArgumentError", "allocate_outputs",
            "LIB_PATH"]

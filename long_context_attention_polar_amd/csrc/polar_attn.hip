@@ -1,12 +1,14 @@
 // Host side of the Polar Attention C ABI: argument checks, per-head constants, launch
-// geometry.  Every check runs before the first HIP call; the library allocates nothing,
-// never synchronises and keeps no mutable global state.
+// geometry.  Every check runs before the first HIP call; the library allocates nothing
+// and never synchronises.  Its one piece of mutable global state is the per-device
+// address of the no-allocation decode's array, looked up once per device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/polar_attn.h"
@@ -546,6 +548,40 @@ polar_status dispatch_bwd(const polar_problem* pr, const polar::BwdParams& bp, v
   return pr->causal ? launch_bwd<128, T, true>(bp, stream) : launch_bwd<128, T, false>(bp, stream);
 }
 
+// ---- no-allocation decode: the split partials live in a file-scope device array.
+// Each GPU the library runs on holds its own copy of `scratch` until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory: the
+// device address is taken once per device with hipGetSymbolAddress, with that device
+// current, and only that address is handed to kernels.
+__device__ __attribute__((aligned(256))) char scratch[POLAR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to (the current device for
+// the null stream), looked up on that device's first call.
+polar_status scratch_on_stream_device(void* stream, void*& ptr) {
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return POLAR_ERR_HIP;
+  if (dev >= kMaxDevices) return POLAR_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = -1;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void* p = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    g_scratch_err[dev] = err;
+    g_scratch_ptr[dev] = err == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return POLAR_ERR_HIP;
+  ptr = g_scratch_ptr[dev];
+  return POLAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -625,9 +661,12 @@ polar_status polar_attn_merge(const polar_problem* pr, const float* partials, in
 }
 
 
-polar_status polar_attn_decode(const polar_problem* pr, const void* q, const void* k_cache, const void* v_cache,
-                               int32_t num_splits, void* workspace, size_t workspace_bytes,
-                               const polar_outputs* out, void* stream) {
+// polar_attn_decode.  use_scratch: the partials go to the library's own device array
+// (the no-allocation entry point), whose device address is looked up only after every
+// check has passed; `workspace` is then ignored.
+static polar_status decode_impl(const polar_problem* pr, const void* q, const void* k_cache, const void* v_cache,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                const polar_outputs* out, void* stream, bool use_scratch) {
   int splits = 0;
   polar_status st = check_decode(pr, num_splits, splits);
   if (st != POLAR_OK) return st;
@@ -642,8 +681,13 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
   if (!q || !k_cache || !v_cache) return POLAR_ERR_NULL_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return POLAR_ERR_MISALIGNED;
   const size_t need = partial_bytes(pr, splits);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return POLAR_ERR_WORKSPACE;
-  if (workspace && !aligned(workspace, 16)) return POLAR_ERR_MISALIGNED;
+  if (use_scratch) {
+    if (need > (size_t)POLAR_NOALLOC_SCRATCH_BYTES) return POLAR_ERR_WORKSPACE;
+    workspace = nullptr;  // not an input of this call: the partials go to the library's array
+  } else {
+    if (need > 0 && (!workspace || workspace_bytes < need)) return POLAR_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 16)) return POLAR_ERR_MISALIGNED;
+  }
   const size_t qb = (size_t)pr->batch * pr->heads * pr->seq_q * pr->head_dim * 2;
   const size_t kvb = (size_t)pr->batch * pr->kv_heads * pr->seq_k * pr->head_dim * 2;
   const void* ins[4] = {q, k_cache, v_cache, workspace};
@@ -654,6 +698,10 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
       overlaps(workspace, need, v_cache, kvb))
     return POLAR_ERR_ALIAS;
   if (pr->heads > 65535 || pr->batch > 65535) return POLAR_ERR_UNSUPPORTED;
+  if (use_scratch) {
+    st = scratch_on_stream_device(stream, workspace);
+    if (st != POLAR_OK) return st;
+  }
   dp.q = q;
   dp.k = k_cache;
   dp.v = v_cache;
@@ -676,6 +724,18 @@ polar_status polar_attn_decode(const polar_problem* pr, const void* q, const voi
     st = launch_split<128>(dp, grid, stream);
   if (st != POLAR_OK) return st;
   return merge_with_lens(pr, (const float*)workspace, splits, nullptr, q, out, stream);
+}
+
+polar_status polar_attn_decode(const polar_problem* pr, const void* q, const void* k_cache, const void* v_cache,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes,
+                               const polar_outputs* out, void* stream) {
+  return decode_impl(pr, q, k_cache, v_cache, num_splits, workspace, workspace_bytes, out, stream, false);
+}
+
+polar_status polar_attn_decode_noalloc(const polar_problem* pr, const void* q, const void* k_cache,
+                                       const void* v_cache, int32_t num_splits, const polar_outputs* out,
+                                       void* stream) {
+  return decode_impl(pr, q, k_cache, v_cache, num_splits, nullptr, 0, out, stream, true);
 }
 
 int32_t polar_attn_decode_paged_num_splits(const polar_problem* pr, const polar_paged_kv* kv, int32_t num_splits) {

@@ -253,6 +253,35 @@ def test_decode_and_merge_validation(lib):
     assert lib.polar_attn_merge(ctypes.byref(pr), fake(10), 4, ctypes.byref(o), None) == 7
 
 
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks like polar_attn_decode, and rejects partials beyond
+    its fixed array with POLAR_ERR_WORKSPACE, before any HIP call."""
+    assert pa.NOALLOC_SCRATCH_BYTES == int(
+        eval(re.search(r"#define POLAR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+             .expand(r"\1 << \2")))
+    o = outputs()
+    big = good_problem(batch=64, heads=8, kv_heads=8, seq_q=1, seq_k=64, head_dim=128)
+    pr, keep = big.to_c()
+    need = lib.polar_attn_decode_workspace_bytes(ctypes.byref(pr), 64)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(pr), fake(1), fake(2), fake(3), 64, ctypes.byref(o), None) == 6
+    # the other checks are those of polar_attn_decode
+    bad = good_problem(seq_q=2, seq_k=1000)
+    bpr, bkeep = bad.to_c()
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(bpr), fake(1), fake(2), fake(3), 0, ctypes.byref(o), None) == 3
+    ok = good_problem(seq_q=1, seq_k=1000, head_dim=128)
+    opr, okeep = ok.to_c()
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(opr), None, fake(2), fake(3), 4, ctypes.byref(o), None) == 1
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(opr), fake(1), fake(2), fake(3), 1001, ctypes.byref(o),
+                                         None) == 2
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(opr), fake(10), fake(2), fake(3), 4, ctypes.byref(o),
+                                         None) == 7
+    empty = good_problem(batch=0, seq_q=1, seq_k=1000, head_dim=128)
+    epr, ekeep = empty.to_c()
+    assert lib.polar_attn_decode_noalloc(ctypes.byref(epr), None, None, None, 0,
+                                         ctypes.byref(pa.PolarOutputs(None, None, None, None, None)), None) == 0
+
+
 def paged(num_blocks=64, block_size=16, max_blocks=64, table=None, lens=None, kp=None, vp=None):
     return pa.PolarPagedKV(fake(2) if kp is None else kp, fake(3) if vp is None else vp,
                            fake(5) if table is None else table, fake(6) if lens is None else lens,
