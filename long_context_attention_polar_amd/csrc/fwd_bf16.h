@@ -32,9 +32,10 @@
 //     still in registers.  Later moves happen only when a row's maximum grows by more
 //     than 16 in base-2 units.  The variant that reports statistics tracks the true
 //     maximum on the side.
-//   * sum p and sum p^2 are taken from the same bf16-rounded weights that enter P V, two
-//     at a time with v_dot2_f32_bf16 (exact products, fp32 sums), as per-lane partial
-//     sums combined once in the epilogue.
+//   * sum p and sum p^2 are summed in fp32 from the fp32 weights, before these are rounded
+//     to bf16 for P V, as per-lane partial sums combined once in the epilogue.  Sums of
+//     the bf16 weights would move n_eff = S1^2 / S2 by up to about 4 * 2^-8 on rows whose
+//     weight mass and squared mass sit on keys rounded in opposite directions.
 //   * Reading variants that change the inner loop are template flags: KF, a per-key
 //     floor (1: weight max(e^s - e^f, 0); 2: e^s only when s > f), for which a row's
 //     reference starts at its floor f so the floor's own weight e^{f - m_ref} never
@@ -50,8 +51,6 @@ namespace polar {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 #define POLAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define POLAR_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
 
@@ -291,9 +290,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             }
       }
     }
-    // ---- a5: p = exp2(c s - m_ref) rounded to bf16 in the B-operand order; the tile's sum p
-    // and sum p^2 are taken from the same bf16 weights, two at a time (exact products,
-    // fp32 sums)
+    // ---- a5: p = exp2(c s - m_ref), rounded to bf16 in the B-operand order; the tile's
+    // sum p and sum p^2 are taken from the fp32 weights
     float t1[NB], t2[NB];
     auto weights = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -307,20 +305,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           if constexpr (KF == POLAR_KEY_FLOOR_GATE) return t > fl ? fast_exp2(t) : 0.0f;
           return fast_exp2(t);
         };
-        float a1 = 0.0f, a2 = 0.0f;  // one dot2 chain per sum
+        float a1 = 0.0f, a2 = 0.0f;  // one chain per sum, over the fp32 weights
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; j += 2) {
-              bf16x2 pp;
-              pp[0] = (__bf16)weight(s[nb][mb][4 * i + j]);
-              pp[1] = (__bf16)weight(s[nb][mb][4 * i + j + 1]);
-              a1 = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, a1, false);
-              a2 = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, a2, false);
-              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = pp[0];
-              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = pp[1];
+              const float w0 = weight(s[nb][mb][4 * i + j]);
+              const float w1 = weight(s[nb][mb][4 * i + j + 1]);
+              a1 += w0;
+              a1 += w1;
+              a2 = fmaf(w0, w0, a2);
+              a2 = fmaf(w1, w1, a2);
+              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)w0;
+              pf[nb][mb * 2 + (i >> 1)][(i & 1) * 4 + j + 1] = (__bf16)w1;
             }
         t1[nb] = a1;
         t2[nb] = a2;
@@ -431,7 +430,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
       for (int e = 0; e < 16; ++e) nn = fmaf(o[nb][dm][e], o[nb][dm][e], nn);
     nn += xor32(nn);
-    const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+    const float inv = nn == 0.0f ? 0.0f : 1.0f / sqrtf(nn);  // a NaN norm stays NaN
     // the data-adaptive floor level needs the norm of the row's q (all lanes take part)
     float sigma = 1.0f;
     if (p.hp.level_form == POLAR_LEVEL_QNORM) {

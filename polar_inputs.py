@@ -209,3 +209,35 @@ def paged_decode_inputs(w: Workload, device):
             pool[rows[b]] = x.view(w.Hkv, mb, bs, w.d).permute(1, 2, 0, 3)
     lens = torch.full((w.B,), w.Tk, dtype=torch.int32, device=dev)
     return q, k_pool, v_pool, rows.to(torch.int32), lens
+
+
+# Rows whose weights sit near bf16 rounding boundaries, for the n_eff precision tests:
+# per head, (strong key value, weak key value) along dimension 0.  With q = e_0 every
+# row's scores are exactly the key values; key 0 scores 0, key 64 scores the strong value
+# and every other key the weak value, so row i sees one key of weight 1, one strong key
+# and i - 1 identical weak keys (the weights relative to the row's maximum in the first
+# 64 keys).  The pairs were picked so that the strong key's and the weak keys' weights,
+# formed in fp32, round to bf16 in opposite directions by nearly half an ulp.
+ROUNDING_PAIRS = {
+    64: ((50.0, -5.03125), (39.5, -10.8125), (50.0, -10.875), (50.0, -4.25)),
+    128: ((56.5, -15.125), (56.5, -7.625), (48.5, -15.375), (24.5, -38.0)),
+}
+
+
+def rounding_adversary_qkv(T, d, seed=0, pairs=None):
+    """q, k, v (bf16, [1, H, T, d]) with one (strong, weak) key-value pair per head as
+    ROUNDING_PAIRS describes; v is N(0,1) from `seed`, and the key dimensions other than
+    0 are N(0,1) too (q is zero there, so they do not change any score)."""
+    pairs = ROUNDING_PAIRS[d] if pairs is None else pairs
+    H = len(pairs)
+    g = torch.Generator().manual_seed(seed)
+    q = torch.zeros(1, H, T, d)
+    q[..., 0] = 1.0
+    k = torch.randn(1, H, T, d, generator=g)
+    v = torch.randn(1, H, T, d, generator=g)
+    for h, (strong, weak) in enumerate(pairs):
+        k[0, h, :, 0] = weak
+        k[0, h, 0, 0] = 0.0
+        if T > 64:
+            k[0, h, 64, 0] = strong
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
