@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64) void polar_merge_kernel(const MergeParams p) {
   for (int e = 0; e < DPL; ++e) nn = fmaf(acc[e], acc[e], nn);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) nn += __shfl_xor(nn, sh, 64);
-  const float inv = nn > 0.0f ? 1.0f / sqrtf(nn) : 0.0f;
+  const float inv = nn == 0.0f ? 0.0f : 1.0f / sqrtf(nn);  // a NaN norm stays NaN
 #pragma unroll
   for (int e = 0; e < DPL; ++e) p.dir[row * D + lane + 64 * e] = acc[e] * inv;
   // the data-adaptive floor level needs the norm of the row's q (all lanes take part)

@@ -171,11 +171,12 @@ __device__ __forceinline__ float null_floor(const HeadParams& hp, int hpi, int n
 //   count = conf * tanh(ln(n_eff) / kappa), or tanh(ln(1 + n_eff) / kappa).
 // m_nat is the row maximum in natural-log units; S1, S2 are relative to exp(m_nat).
 // With a per-key floor S1 may be 0 (no key above the floor): every channel is then 0.
+// A NaN in the statistics (from a NaN input the row sees) reaches every channel.
 __device__ __forceinline__ void magnitude_channel(const HeadParams& hp, int hpi, float m_nat, float S1, float S2,
                                                   float f, bool floor_on, float& neff, float& conf,
                                                   float& count) {
 #pragma clang fp contract(off)
-  if (!(S1 > 0.0f)) {
+  if (S1 == 0.0f) {
     neff = conf = count = 0.0f;
     return;
   }

@@ -92,8 +92,9 @@ def finish_rows(m, s1, s2, acc, n, lam, beta, kappa: float):
     m, s1, s2, acc = _f64(m), _f64(s1), _f64(s2), _f64(acc)
     n_eff = s1 * s1 / s2
     norm = np.sqrt(np.sum(acc * acc, axis=-1))
-    safe = np.where(norm > 0.0, norm, 1.0)
-    direction = np.where(norm[:, None] > 0.0, acc / safe[:, None], 0.0)
+    # u = 0 exactly where acc = 0 (reading A-10); a NaN in acc stays NaN
+    safe = np.where(norm == 0.0, 1.0, norm)
+    direction = np.where(norm[:, None] == 0.0, 0.0, acc / safe[:, None])
     if beta is None:
         conf = np.ones_like(s1)
     else:

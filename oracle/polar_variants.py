@@ -117,7 +117,7 @@ def _channels(m: float, s1: float, s2: float, acc, f: float, floor_on: bool, kap
         out.update(n_eff=0.0, confidence=0.0, count=0.0)
         return out
     norm = float(np.sqrt(acc @ acc))
-    if norm > 0.0:
+    if norm != 0.0:  # u = 0 where acc = 0; a NaN in acc stays NaN
         out["direction"] = acc / norm
     n_eff = s1 * s1 / s2
     conf = 1.0 / (1.0 + math.exp(f - m - math.log(s1))) if floor_on else 1.0

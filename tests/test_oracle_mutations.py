@@ -36,7 +36,7 @@ MUTATIONS = {
     "merge weight on S2 not squared": ("s2 += w * w * b2", "s2 += w * b2"),
     "merge weight on acc squared": ("acc = acc + w * c", "acc = acc + w * w * c"),
     "kv head mapping modulo": ("hk = h // group", "hk = h % Hkv"),
-    "direction divided by S1": ("direction = np.where(norm[:, None] > 0.0, acc / safe[:, None], 0.0)",
+    "direction divided by S1": ("direction = np.where(norm[:, None] == 0.0, 0.0, acc / safe[:, None])",
                                 "direction = acc / s1[:, None]"),
     "max not subtracted consistently": ("p = np.exp(s - m[:, None])", "p = np.exp(s)"),
 }
