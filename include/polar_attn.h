@@ -53,6 +53,17 @@
  *   Empty      batch == 0 or seq_q == 0 is valid and enqueues nothing; the data
  *              pointers of such a call may be NULL (polar_attn_bwd with seq_q == 0
  *              still writes zero dk and dv).
+ *   Values     The operator is defined for finite q, k, v; the library does not
+ *              inspect values.  A NaN propagates through the forward and decode entry
+ *              points: a NaN in q_i makes every output channel of row i NaN; one in
+ *              k_j, every channel of every row that sees key j; one in v_j, the
+ *              direction of every row that sees key j, and possibly the direction of
+ *              earlier rows computed in the same query tile (a zero weight times NaN),
+ *              while n_eff, confidence and count do not depend on v.  In the
+ *              statistics of an affected row S1 and S2 are NaN and m is unspecified.
+ *              Every other row is exactly what it is without the NaN.  Infinite inputs
+ *              give unspecified values in the rows they reach and leave the other rows
+ *              unchanged.  The backward entry points make no statement on them.
  */
 #ifndef POLAR_ATTN_H
 #define POLAR_ATTN_H
@@ -375,8 +386,10 @@ polar_status polar_attn_bwd_saved(const polar_problem* problem, const void* q, c
                                   const float* saved, const polar_grads* grads, float* dq, float* dk, float* dv,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static description of a status code. */
-const char* polar_status_string(polar_status status);
+/* Static description of a status code: any int32 value is accepted (a value that is no
+ * polar_status gives "unknown status"; the parameter is an int32_t so that such a value
+ * is well-defined input in C and C++ alike). */
+const char* polar_status_string(int32_t status);
 
 /* POLAR_ABI_VERSION of the built library. */
 int32_t polar_abi_version(void);

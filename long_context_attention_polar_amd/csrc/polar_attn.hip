@@ -57,7 +57,6 @@ constexpr int kBf16Nb_d64 = POLAR_BF16_NB_D64;    // 32-row query blocks per wav
 constexpr int kBf16Nb_d128 = POLAR_BF16_NB_D128;
 constexpr int kBf16Occ_d64 = POLAR_BF16_OCC_D64;  // waves per SIMD the registers must allow
 constexpr int kBf16Occ_d128 = POLAR_BF16_OCC_D128;
-constexpr int kF32Rows = 128;                         // query rows per workgroup, fp32 path
 // Decode launch geometry.
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeUnroll = 8;
@@ -240,10 +239,11 @@ polar_status launch_fwd(const polar_problem* pr, FwdParams& fp, void* stream) {
     if (fp.stats || fp.part) return launch_bf16<D, CAUSAL, true>(fp, (unsigned)blocks, stream);
     return launch_bf16<D, CAUSAL, false>(fp, (unsigned)blocks, stream);
   }
-  fp.n_qt = (pr->seq_q + kF32Rows - 1) / kF32Rows;
+  fp.n_qt = (pr->seq_q + polar::kF32RowsPerBlock - 1) / polar::kF32RowsPerBlock;
   const long long blocks = (long long)fp.n_qt * BH;
   if (blocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-  return launch(polar::polar_fwd_f32_kernel<D, CAUSAL>, dim3((unsigned)blocks), dim3(kF32Rows), fp, stream);
+  return launch(polar::polar_fwd_f32_kernel<D, CAUSAL>, dim3((unsigned)blocks), dim3(polar::kF32Threads), fp,
+                stream);
 }
 
 // Query heads one grouped-decode workgroup serves: the largest of 8, 4, 2, 1 that divides
@@ -588,7 +588,8 @@ extern "C" {
 
 int32_t polar_abi_version(void) { return POLAR_ABI_VERSION; }
 
-const char* polar_status_string(polar_status s) {
+const char* polar_status_string(int32_t s) {
+  // the argument is an int: a value outside polar_status is valid input here
   switch (s) {
     case POLAR_OK: return "ok";
     case POLAR_ERR_NULL_ARG: return "a required pointer is NULL";

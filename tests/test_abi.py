@@ -20,6 +20,11 @@ HEADER = os.path.join(ROOT, "include", "polar_attn.h")
 
 @pytest.fixture(scope="module")
 def lib():
+    # POLAR_TEST_LIB: another build of the library to run these checks against (the
+    # host-sanitizer build of tests/test_host_sanitizers.py)
+    path = os.environ.get("POLAR_TEST_LIB")
+    if path:
+        return pa.load_library(path)
     if not os.path.exists(pa.LIB_PATH):
         pbuild.build()
     return pa.load_library()

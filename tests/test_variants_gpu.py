@@ -69,20 +69,25 @@ def decidable_rows(q, k, causal, kw, variant, rows=None):
     return ok
 
 
-def soft_floor_condition(q, k, causal, kw, variant):
-    """[B, H, Tq] condition numbers of S1 and S2 under the soft per-key floor.
+def soft_floor_condition(q, k, causal, kw, variant, v=None):
+    """[B, H, Tq] condition numbers of S1 and S2 (and, given v, of the direction) under
+    the soft per-key floor.
 
     A weight e^s - e^f near the floor is ill-conditioned in the score: a score error
     delta changes it by about e^s delta while the weight itself is e^s - e^f.  With score
     errors bounded by u (1 + |s|), the relative errors of S1 and S2 are bounded by
     u kappa1 and u kappa2, kappa1 = sum e^{s - m} (1 + |s|) / S1 and
-    kappa2 = 2 max(w) sum e^{s - m} (1 + |s|) / S2, the sums over the keys above the floor."""
+    kappa2 = 2 max(w) sum e^{s - m} (1 + |s|) / S2, and the direction's error by u kappa_u,
+    kappa_u = sum e^{s - m} (1 + |s|) ||v_j|| / ||acc||, the sums over the keys above the
+    floor."""
     var = variant_of(variant)
     q, k = to_np(q), to_np(k)
+    v = None if v is None else to_np(v)
     B, H, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     k1 = np.ones((B, H, Tq))
     k2 = np.ones((B, H, Tq))
+    ku = np.ones((B, H, Tq))
     scale = 1.0 / math.sqrt(d)
     for b in range(B):
         for h in range(H):
@@ -101,16 +106,26 @@ def soft_floor_condition(q, k, causal, kw, variant):
                 if not above.any():
                     continue
                 w = np.exp(s[above] - m) - np.exp(f - m)
-                gross = float(np.sum(np.exp(s[above] - m) * (1.0 + np.abs(s[above]))))
+                e = np.exp(s[above] - m) * (1.0 + np.abs(s[above]))
+                gross = float(np.sum(e))
                 k1[b, h, i] = max(1.0, gross / w.sum())
                 k2[b, h, i] = max(1.0, 2.0 * w.max() * gross / np.sum(w * w))
-    return k1, k2
+                if v is not None:
+                    vv = v[b, h // (H // Hkv), lo:hi][above]
+                    acc = w @ vv
+                    norm = float(np.sqrt(acc @ acc))
+                    if norm > 0.0:
+                        ku[b, h, i] = max(1.0, float(e @ np.sqrt(np.sum(vv * vv, axis=1))) / norm)
+    return (k1, k2) if v is None else (k1, k2, ku)
 
 
 def compare(out, ref, kind, ok, label, cond=None):
     """assert_parity on the decidable rows (rows with n_eff = 0 compared exactly).  With
-    `cond` (the soft floor's condition numbers of S1 and S2) the statistics S1, S2 are
-    checked against the tolerance times the row's condition number."""
+    `cond` (the soft floor's condition numbers of S1 and S2, and of the direction) the
+    statistics S1, S2 are checked against the tolerance times the row's condition number,
+    and so are the channels, each by the condition of what it is formed from:
+    n_eff = S1^2 / S2 by 2 kappa1 + kappa2, the confidence by kappa1, the count by
+    3 kappa1 + kappa2, the direction by kappa_u (never below the plain tolerance)."""
     assert ok.mean() >= 0.9, f"{label}: only {ok.mean():.2f} of the rows are decidable"
     flat = lambda x: x.reshape(-1, *x.shape[3:])
     g = {key: to_np(t) for key, t in out.items() if torch.is_tensor(t) and key != "partials"}
@@ -123,8 +138,23 @@ def compare(out, ref, kind, ok, label, cond=None):
     keys = [key for key in g if not (cond is not None and key == "stats")]
     sub_g = {key: torch.from_numpy(flat(g[key])[live][None, None]) for key in keys}
     sub_r = {key: flat(v)[live][None, None] for key, v in ref.items()}
-    if live.any():
+    if live.any() and cond is not None and len(cond) == 3:
+        tol = TOL[kind]
+        k1, k2, ku = (flat(c)[live] for c in cond)
+        du = np.sqrt(((flat(g["direction"])[live] - flat(ref["direction"])[live]) ** 2).sum(-1))
+        en = np.abs(flat(g["n_eff"])[live] - flat(ref["n_eff"])[live]) / flat(ref["n_eff"])[live]
+        ec = np.abs(flat(g["confidence"])[live] - flat(ref["confidence"])[live])
+        et = np.abs(flat(g["count"])[live] - flat(ref["count"])[live])
+        for name, err, allow in (("direction", du, tol["direction"] * ku), ("n_eff", en, tol["n_eff"] * (2 * k1 + k2)),
+                                 ("confidence", ec, tol["confidence"] * k1),
+                                 ("count", et, tol["count"] * (3 * k1 + k2))):
+            assert np.isfinite(err).all() and np.all(err <= allow), \
+                f"{label} {name}: worst {err.max():.3e}, worst ratio to the conditioned tolerance {(err / allow).max():.3f}"
+        for key in ("direction", "n_eff"):
+            assert torch.isfinite(out[key]).all(), f"{label} non-finite {key}"
+    elif live.any():
         assert_parity(sub_g, sub_r, kind, label=label)
+    if live.any():
         if cond is not None and "stats" in g:
             tol = TOL[kind]
             st = flat(g["stats"])[live]
@@ -148,7 +178,7 @@ def test_prefill_variant(name, d, dtype):
     out = pa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, stats=True, variant=variant, **H4)
     torch.cuda.synchronize()
     ok = decidable_rows(q, k, True, H4, variant)
-    cond = soft_floor_condition(q, k, True, H4, variant) if variant.get("key_floor") == "soft" else None
+    cond = soft_floor_condition(q, k, True, H4, variant, v) if variant.get("key_floor") == "soft" else None
     compare(out, ref, "bf16" if dtype == torch.bfloat16 else "f32", ok, f"prefill {name} d={d} {dtype}", cond)
 
 
