@@ -53,6 +53,7 @@ CHUNKED = f"bf16_chunked_prefill_b1_h16_t65536_d64_chunk{CHUNK}"
 SOFT_FLOOR = "bf16_b1_h16_t65536_d64_soft_key_floor"
 WIN = 4096
 NEEDLE = "bf16_b4_h8_t4096_d64_needle"
+FP32_SMALL = "fp32_b1_h2_t256_d64"
 WINDOW = f"bf16_b1_h16_t65536_d64_window{WIN}"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
@@ -63,6 +64,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = {
     "fwd_bf16_t65536_d64": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
     "fwd_bf16_t16384_d128": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
+    "fwd_bf16_needle_b4_h8_t4096_d64": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
+    "fwd_f32_b1_h2_t256_d64": (["fwd_f32.h"], "polar_fwd_f32_kernel"),
     "decode_b64_h8_tk65536_d128": (["decode.h"], "polar_decode_split_kernel"),
     "merge_b64_h8_d128": (["decode.h"], "polar_merge_kernel"),
     "paged_gqa_decode_b64_h32_kv8_tk65536_d128": (["decode_group.h", "decode.h"], "polar_decode_group_kernel"),
@@ -188,13 +191,17 @@ def measured_traffic(kernel_key):
     return profiled(kernel_key, "hbm_bytes_per_launch")
 
 
+def _oracle_threads():
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+
+
 def cpu_baseline(seconds):
     """The fp64 oracle, as it is, on a bounded sample of the 16K prefill workload: whole
     heads, each in blocks of 512 query rows, until about `seconds` of wall time have
     passed (the rate is taken over the blocks done)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
 
     import polar_inputs as pin
     from oracle import polar_attention
@@ -217,11 +224,96 @@ def cpu_baseline(seconds):
         heads_done += 1
         if dt >= seconds:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    threads = _oracle_threads()
     return {"value": 4 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 NumPy oracle on {heads_done} of {w.H} heads ({rows_done} query rows, {pairs} causal "
                       f"(query,key) pairs) of the T=16384 d=128 prefill, {dt:.1f} s; host os.cpu_count()="
-                      f"{os.cpu_count()}, BLAS threads={threads}, torch threads={torch.get_num_threads()}"}
+                      f"{os.cpu_count()}, BLAS threads={threads}, torch threads={torch.get_num_threads()}",
+            "_pairs": pairs, "_seconds": dt}
+
+
+def oracle_per_config(c3_sample, gpu_ms, decode_inputs):
+    """The fp64 oracle timed on every configuration: whole for the two small ones, on a
+    bounded sample for the others, scaled to the whole configuration by its (query, key)
+    pairs (the oracle's work is proportional to them: one row block costs its rows times
+    its visible keys).  `c3_sample` is the 16K prefill sample of cpu_baseline; the decode
+    sample takes a few (sequence, head) slices copied from the device-resident cache."""
+    import numpy as np
+
+    import polar_inputs as pin
+    from oracle import polar_attention
+
+    def run(w, q, k, v, h0, h1, rows=None, b0=0, b1=None):
+        b1 = w.B if b1 is None else b1
+        q = q[b0:b1, h0:h1].float().numpy().astype(np.float64)
+        kv = (h0 // (w.H // w.Hkv), (h1 - 1) // (w.H // w.Hkv) + 1)
+        k = k[b0:b1, kv[0]:kv[1]].float().numpy().astype(np.float64)
+        v = v[b0:b1, kv[0]:kv[1]].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        polar_attention(q, k, v, causal=w.causal, len_temp=w.len_temp()[h0:h1],
+                        null_bias=None if w.null_bias() is None else w.null_bias()[h0:h1],
+                        count_scale=w.count_scale()[h0:h1], rows=rows)
+        return time.perf_counter() - t0
+
+    out = []
+
+    def entry(name, sample, pairs_done, secs):
+        w = pin.WORKLOADS[name]
+        full = secs * w.pairs() / pairs_done
+        e = {"workload": name, "sample": sample, "sample_s": round(secs, 3),
+             "oracle_s_full": round(full, 3), "extrapolated": pairs_done != w.pairs()}
+        if gpu_ms.get(name):
+            e["gpu_ms"] = gpu_ms[name]
+            e["oracle_over_gpu"] = round(full * 1e3 / gpu_ms[name], 1)
+        out.append(e)
+
+    for name in (FP32_SMALL, NEEDLE):
+        w = pin.WORKLOADS[name]
+        q, k, v, _ = pin.workload_inputs(w, "cpu")
+        entry(name, "every row", w.pairs(), run(w, q, k, v, 0, w.H))
+    entry(PREFILL[0], c3_sample["sample"], c3_sample["_pairs"], c3_sample["_seconds"])
+    # 64K prefill: blocks of 512 rows at four places along the sequence, in two heads
+    w = pin.WORKLOADS[PREFILL[1]]
+    q, k, v, _ = pin.workload_inputs(w, "cpu")
+    secs, pairs = 0.0, 0
+    for h in (0, w.H - 1):
+        for end in (w.Tq // 4, w.Tq // 2, 3 * w.Tq // 4, w.Tq):
+            rows = np.arange(end - 512, end)
+            secs += run(w, q, k, v, h, h + 1, rows=rows)
+            pairs += int((rows + 1).sum())
+    entry(PREFILL[1], "rows [T/4-512, T/4), [T/2-512, T/2), [3T/4-512, 3T/4), [T-512, T) of heads 0 and 15",
+          pairs, secs)
+    # decode: four (sequence, head) slices of the 64K cache
+    w = pin.WORKLOADS[DECODE]
+    qd, kd, vd = decode_inputs
+    secs, pairs = 0.0, 0
+    for b, h in ((0, 0), (21, 3), (42, 5), (63, 7)):
+        secs += run(w, qd[b:b + 1].cpu(), kd[b:b + 1].cpu(), vd[b:b + 1].cpu(), h, h + 1)
+        pairs += w.Tk
+    entry(DECODE, "4 of the 512 (sequence, head) rows: (0,0), (21,3), (42,5), (63,7)", pairs, secs)
+    return out
+
+
+def _percentile(sorted_ms, pct):
+    """Linear-interpolated percentile of an ascending list."""
+    x = (len(sorted_ms) - 1) * pct / 100.0
+    i = int(x)
+    j = min(i + 1, len(sorted_ms) - 1)
+    return sorted_ms[i] + (sorted_ms[j] - sorted_ms[i]) * (x - i)
+
+
+def rocm_version():
+    """ROCm release of the installation, and the HIP version torch was built with."""
+    ver = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                ver = f.read().strip()
+            break
+        except OSError:
+            pass
+    import torch
+    return {"rocm": ver, "torch_hip": torch.version.hip, "torch": torch.__version__}
 
 
 def main():
@@ -285,6 +377,13 @@ def main():
     kwn = dict(causal=True, len_temp=wn.len_temp(), null_bias=wn.null_bias(), count_scale=wn.count_scale())
     parts.append(dict(name=NEEDLE, w=wn, kind="side", flops=prefill_flops(wn), headline=False, separate=True,
                       run=lambda: pa.fwd(qn, kn, vn, out=outn, **kwn)))
+    # the fp32 workload (B=1, H=2, T=256, d=64): launch-bound, correctness path
+    w1 = pin.WORKLOADS[FP32_SMALL]
+    q1, k1, v1, _ = pin.workload_inputs(w1, dev)
+    out1 = pa.allocate_outputs(w1.B, w1.H, w1.Tq, w1.d, dev)
+    kw1 = dict(causal=True, len_temp=w1.len_temp(), null_bias=w1.null_bias(), count_scale=w1.count_scale())
+    parts.append(dict(name=FP32_SMALL, w=w1, kind="side", flops=prefill_flops(w1), headline=False, separate=True,
+                      run=lambda: pa.fwd(q1, k1, v1, out=out1, **kw1)))
     parts.append(dict(name=WINDOW, w=wl, kind="side", flops=4 * wl.d * wl.B * wl.H * window_pairs(wl.Tq, WIN),
                       headline=False, separate=True,
                       run=lambda: pa.fwd(ql, kl, vl, out=outl, variant={"window": WIN}, **kwl)))
@@ -367,7 +466,8 @@ def main():
         ms = [a.elapsed_time(b) for a, b in events[p["name"]]]
         ms.sort()
         avg = sum(ms) / len(ms)
-        entry = {"ms_avg": avg, "ms_median": ms[len(ms) // 2], "ms_min": ms[0], "ms_max": ms[-1]}
+        entry = {"ms_avg": avg, "ms_median": ms[len(ms) // 2], "ms_p10": _percentile(ms, 10),
+                 "ms_p90": _percentile(ms, 90), "ms_min": ms[0], "ms_max": ms[-1]}
         if p["kind"] == "prefill":
             entry["tflops"] = p["flops"] / (avg * 1e-3) / 1e12
             entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
@@ -430,7 +530,11 @@ def main():
                                     "the merge; the one-pass prefill's algorithmic flops"},
         "needle_prefill": {"bound": "mfma", "achieved": res[NEEDLE]["tflops"], "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": res[NEEDLE]["frac_bf16_peak"], "ms": res[NEEDLE]["ms_avg"],
+                           "mfma_busy": profiled("fwd_bf16_needle_b4_h8_t4096_d64", "mfma_busy"),
+                           "clock_ghz": profiled("fwd_bf16_needle_b4_h8_t4096_d64", "clock_ghz"),
                            "note": "bf16 B=4 H=8 T=4096 d=64 causal, one planted needle per head"},
+        "fp32_prefill": {"bound": "alu", "achieved": res[FP32_SMALL]["tflops"], "ms": res[FP32_SMALL]["ms_avg"],
+                         "note": "fp32 B=1 H=2 T=256 d=64 causal: a correctness path, launch-bound at this size"},
         "variants": {
             "soft_key_floor": {"bound": "mfma", "achieved": res[SOFT_FLOOR]["tflops"], "peak": PEAK_BF16_TFLOPS,
                                "unit": "TFLOP/s", "frac": res[SOFT_FLOOR]["frac_bf16_peak"],
@@ -446,10 +550,17 @@ def main():
                                    "(polar_attn_bwd_saved): row constants, dq, dk, dv"},
         "parts": res,
         "source_digest": digest,
+        "software": rocm_version(),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        base = cpu_baseline(args.cpu_seconds)
+        gpu_ms = {name: res[name]["ms_avg"] for name in (FP32_SMALL, NEEDLE, *PREFILL, DECODE)}
+        print("[bench] timing the CPU oracle per configuration", file=sys.stderr, flush=True)
+        base["per_config"] = oracle_per_config(base, gpu_ms, (qd, kd, vd))
+        base.pop("_pairs")
+        base.pop("_seconds")
+        line["cpu_baseline"] = base
     print(json.dumps(line), flush=True)
 
 
