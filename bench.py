@@ -62,9 +62,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 # and the launch-geometry constants of the host file), and the kernel's name, whose
 # template arguments in the host file's dispatch lines are part of its build.
 KERNEL_SOURCES = {
-    "fwd_bf16_t65536_d64": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
-    "fwd_bf16_t16384_d128": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
-    "fwd_bf16_needle_b4_h8_t4096_d64": (["fwd_bf16.h"], "polar_fwd_bf16_kernel"),
+    "fwd_bf16_t65536_d64": (["fwd_bf16_pipe.h", "fwd_bf16.h"], "polar_fwd_bf16_pipe_kernel"),
+    "fwd_bf16_t16384_d128": (["fwd_bf16_pipe.h", "fwd_bf16.h"], "polar_fwd_bf16_pipe_kernel"),
+    "fwd_bf16_needle_b4_h8_t4096_d64": (["fwd_bf16_pipe.h", "fwd_bf16.h"], "polar_fwd_bf16_pipe_kernel"),
     "fwd_f32_b1_h2_t256_d64": (["fwd_f32.h"], "polar_fwd_f32_kernel"),
     "decode_b64_h8_tk65536_d128": (["decode.h"], "polar_decode_split_kernel"),
     "merge_b64_h8_d128": (["decode.h"], "polar_merge_kernel"),
@@ -490,15 +490,20 @@ def main():
     digest = source_digest()
     big = res[PREFILL[1]]
     roofline = {"bound": "mfma", "achieved": big["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": big["tflops"] / PEAK_BF16_TFLOPS, "kernel": "polar_fwd_bf16_kernel<64,...> (T=65536 d=64)",
+                "frac": big["tflops"] / PEAK_BF16_TFLOPS, "kernel": "polar_fwd_bf16_pipe_kernel<64,...> (T=65536 d=64)",
                 "traffic": measured_traffic("fwd_bf16_t65536_d64"),
                 # from the committed counter profile of this kernel: matrix-core busy cycles
                 # over the dispatch's active cycles, and the clock it ran at
                 "mfma_busy": profiled("fwd_bf16_t65536_d64", "mfma_busy"),
-                "clock_ghz": profiled("fwd_bf16_t65536_d64", "clock_ghz")}
+                "clock_ghz": profiled("fwd_bf16_t65536_d64", "clock_ghz"),
+                # the vector ALU's share of the SIMD cycles: at d=64 it, not the matrix cores,
+                # is the saturated unit (about 9.7 VALU instructions per MFMA, two of them exp)
+                "valu_busy": profiled("fwd_bf16_t65536_d64", "valu_busy"),
+                "mfma_valu_coexec": profiled("fwd_bf16_t65536_d64", "mfma_valu_coexec")}
     small = res[PREFILL[0]]
     small.update({"mfma_busy": profiled("fwd_bf16_t16384_d128", "mfma_busy"),
                   "clock_ghz": profiled("fwd_bf16_t16384_d128", "clock_ghz"),
+                  "valu_busy": profiled("fwd_bf16_t16384_d128", "valu_busy"),
                   "traffic": measured_traffic("fwd_bf16_t16384_d128")})
     dec = res[DECODE]
     decode_roof = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -249,21 +249,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
   };
 
-  __syncthreads();
+  publish_tiles();
   for (int t = 0; t < ntiles; t += 2) {
     if (t + 1 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 1) * BN, voff, k_buf1, wave);
       load_tile<D, BN, NW>(vb, (t + 1) * BN, voff, v_buf1, wave);
     }
     if (t * BN <= wave_kmax) compute_tile(k_buf0, v_buf0, t * BN);
-    __syncthreads();
+    publish_tiles();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 2) * BN, voff, k_buf0, wave);
       load_tile<D, BN, NW>(vb, (t + 2) * BN, voff, v_buf0, wave);
     }
     if ((t + 1) * BN <= wave_kmax) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
-    __syncthreads();
+    publish_tiles();
   }
 
   if (!live) return;
@@ -467,15 +467,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     if (t_lo >= ntiles) continue;  // none of this head's tiles in the run (uniform)
     __syncthreads();  // the previous head's last tile is no longer read
     load(t_lo, q_buf0, w_buf0, r_buf0);
-    __syncthreads();
+    publish_tiles();
     for (int t = t_lo; t < ntiles; t += 2) {
       if (t + 1 < ntiles) load(t + 1, q_buf1, w_buf1, r_buf1);
       if (!CAUSAL || t * BQ + BQ - 1 + off >= wk0) compute_tile(q_buf0, w_buf0, r_buf0, t * BQ);
-      __syncthreads();
+      publish_tiles();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) load(t + 2, q_buf0, w_buf0, r_buf0);
       if (!CAUSAL || (t + 1) * BQ + BQ - 1 + off >= wk0) compute_tile(q_buf1, w_buf1, r_buf1, (t + 1) * BQ);
-      __syncthreads();
+      publish_tiles();
     }
   }
 

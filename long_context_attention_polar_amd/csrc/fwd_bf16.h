@@ -102,6 +102,16 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int kv0, 
   }
 }
 
+// Make the tile loads of every wave visible to the workgroup: wait for this wave's own
+// global->LDS loads (vmcnt), then the barrier.  The explicit wait is needed because the
+// compiler's workgroup barrier does not wait for these loads by itself: their LDS writes
+// are not ordered by the barrier's memory fence, and without the wait a wave may read a
+// tile that another wave's loads have not finished writing.
+__device__ __forceinline__ void publish_tiles() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __syncthreads();
+}
+
 template <int D, int BN, int NW, int NB, int OCC, bool CAUSAL, bool STATS, int KF = POLAR_KEY_FLOOR_NULL,
           bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_fwd_bf16_kernel(
@@ -396,21 +406,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   };
 
   // ---- main loop: tile t is read from one buffer pair while tile t+1 loads into the other
-  __syncthreads();
+  publish_tiles();
   for (int t = t_begin; t < ntiles; t += 2) {
     if (t + 1 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 1) * BN, voff, k_buf1, wave);
       load_tile<D, BN, NW>(vb, (t + 1) * BN, voff, v_buf1, wave);
     }
     if (wave_needs(t * BN)) compute_tile(k_buf0, v_buf0, t * BN);
-    __syncthreads();
+    publish_tiles();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) {
       load_tile<D, BN, NW>(kb, (t + 2) * BN, voff, k_buf0, wave);
       load_tile<D, BN, NW>(vb, (t + 2) * BN, voff, v_buf0, wave);
     }
     if (wave_needs((t + 1) * BN)) compute_tile(k_buf1, v_buf1, (t + 1) * BN);
-    __syncthreads();
+    publish_tiles();
   }
 
   // ---- a7: combine the two halves of each row and form the channels [ATMA §2.1].

@@ -17,6 +17,7 @@
 #include "decode.h"
 #include "decode_group.h"
 #include "fwd_bf16.h"
+#include "fwd_bf16_pipe.h"
 #include "fwd_f32.h"
 #include "polar_common.h"
 
@@ -210,6 +211,9 @@ polar_status launch_bf16_kf(const FwdParams& fp, unsigned blocks, void* stream) 
       return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, true>, dim3(blocks),
                     dim3(kBf16Waves * 64), fp, stream);
   }
+  if constexpr (KF == POLAR_KEY_FLOOR_NULL)
+    return launch(polar::polar_fwd_bf16_pipe_kernel<D, kBf16Waves, NB, OCC, CAUSAL, STATS>, dim3(blocks),
+                  dim3(kBf16Waves * 64), fp, stream);
   return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, false>, dim3(blocks),
                 dim3(kBf16Waves * 64), fp, stream);
 }
