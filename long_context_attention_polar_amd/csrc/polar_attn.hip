@@ -58,6 +58,7 @@ constexpr int kBf16Nb_d64 = POLAR_BF16_NB_D64;    // 32-row query blocks per wav
 constexpr int kBf16Nb_d128 = POLAR_BF16_NB_D128;
 constexpr int kBf16Occ_d64 = POLAR_BF16_OCC_D64;  // waves per SIMD the registers must allow
 constexpr int kBf16Occ_d128 = POLAR_BF16_OCC_D128;
+constexpr int kBf16Occ_d64_one_round = 3;           // one 32-row block per wave: 160 registers
 // Decode launch geometry.
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeUnroll = 8;
@@ -200,6 +201,13 @@ polar_status check_entry_variant(const polar_problem* pr, const HeadParams& hp, 
   }
 }
 
+// Workgroups of the bf16 prefill resident at once: 256 CUs x 4 SIMDs x OCC waves per SIMD,
+// kBf16Waves waves each.
+template <int OCC>
+constexpr int kResidentWorkgroups() {
+  return 256 * 4 * OCC / kBf16Waves;
+}
+
 // bf16 prefill with the key-floor and window flags of the variant.
 template <int D, bool CAUSAL, bool STATS, int KF>
 polar_status launch_bf16_kf(const FwdParams& fp, unsigned blocks, void* stream) {
@@ -211,9 +219,26 @@ polar_status launch_bf16_kf(const FwdParams& fp, unsigned blocks, void* stream) 
       return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, true>, dim3(blocks),
                     dim3(kBf16Waves * 64), fp, stream);
   }
-  if constexpr (KF == POLAR_KEY_FLOOR_NULL)
+  if constexpr (KF == POLAR_KEY_FLOOR_NULL) {
+    // A causal grid the chip holds in one round lasts as long as its heaviest query tile;
+    // at d = 64 such grids take query tiles of half the rows (one 32-row block per wave,
+    // 160 registers, so three waves per SIMD), which the heaviest-first order spreads over
+    // more resident slots.  Larger grids, and every non-causal one (equal tiles), keep two
+    // blocks per wave, which share each K and V operand read between two MFMAs.
+    if constexpr (D == 64 && NB == 2 && CAUSAL) {
+      if (blocks <= (unsigned)kResidentWorkgroups<OCC>()) {
+        FwdParams f1 = fp;
+        constexpr int BM1 = kBf16Waves * 32;
+        f1.n_qt = (fp.Tq + BM1 - 1) / BM1;
+        const unsigned blocks1 = (unsigned)f1.n_qt * (unsigned)(fp.B * fp.H);
+        return launch(polar::polar_fwd_bf16_pipe_kernel<D, kBf16Waves, 1, kBf16Occ_d64_one_round, CAUSAL, STATS>,
+                      dim3(blocks1),
+                      dim3(kBf16Waves * 64), f1, stream);
+      }
+    }
     return launch(polar::polar_fwd_bf16_pipe_kernel<D, kBf16Waves, NB, OCC, CAUSAL, STATS>, dim3(blocks),
                   dim3(kBf16Waves * 64), fp, stream);
+  }
   return launch(polar::polar_fwd_bf16_kernel<D, BN, kBf16Waves, NB, OCC, CAUSAL, STATS, KF, false>, dim3(blocks),
                 dim3(kBf16Waves * 64), fp, stream);
 }

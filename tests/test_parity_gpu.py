@@ -67,6 +67,17 @@ def test_fwd_gqa_and_bottom_right_causal(dtype):
     run_case(1, 2, 2, 70, 333, 64, dtype, False, seed=13, beta=[0.0] * 2, label="Tq<Tk")
 
 
+@pytest.mark.parametrize("stats", [True, False])
+@pytest.mark.parametrize("B,H,Tq,Tk", [(2, 16, 4100, 4100), (3, 16, 3000, 3300)])
+def test_fwd_two_block_causal_path_ragged(B, H, Tq, Tk, stats):
+    """Causal d=64 grids too large for one resident round keep two 32-row blocks per wave
+    (smaller causal grids take one block per wave); these shapes reach that path with a
+    ragged last query tile and a ragged last key tile, and (second case) bottom-right
+    alignment with more keys than queries.  Every row against the oracle."""
+    run_case(B, H, H, Tq, Tk, 64, torch.bfloat16, True, seed=Tq + Tk + B, beta=[0.0] * H, stats=stats,
+             label=f"two-block causal B={B} H={H} Tq={Tq} Tk={Tk} stats={stats}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Hkv,T", [(1, 8, 8, 1000), (1, 8, 2, 700), (2, 8, 4, 520), (1, 16, 16, 300),
                                        (1, 8, 8, 4096)])
