@@ -17,10 +17,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["polar_attn.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 vector instructions are disabled in the device code of every HIP translation
-# unit (-Xarch_device: the host compiler does not know the feature and would warn).
-HIP_FLAGS = ["-Xarch_device", "-Xclang", "-Xarch_device", "-target-feature",
-             "-Xarch_device", "-Xclang", "-Xarch_device", "-packed-fp32-ops"]
+# Packed fp32 vector instructions are disabled for every HIP translation unit.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:
