@@ -13,12 +13,13 @@
 //          B-operand key order; dQ^T += K^T (cl dS)^T with K^T read from the row-major K
 //          tile by transpose reads;
 //   dk/dv  per key tile, over the query rows of every query head of its GQA group:
-//          S = Q K^T and G = W V^T (Q, W rows from LDS, K and V in registers, lane = key);
+//          S = Q K^T and G = W V^T (Q, W rows from LDS, K in registers, lane = key);
 //          P and cl dS with the per-row constants read from LDS; dK^T += Q^T (cl dS) and
-//          dV^T += W^T P with Q^T and W^T from transpose reads.  At d = 128 the four
-//          accumulators and the K, V fragments do not fit one wave's share of two waves per
-//          SIMD, so dk (S, G, dK) and dv (S, dV) run as two kernels that each keep two
-//          waves per SIMD; S is computed in both.  Under a causal mask the first key
+//          dV^T += W^T P with Q^T and W^T from transpose reads.  The V operand of G sits
+//          in registers at d = 64; at d = 128 the four accumulators and both K and V
+//          fragments would not fit one wave's share of two waves per SIMD, so the
+//          workgroup's 128 V rows are loaded once into LDS and G reads its V operand
+//          from there, which keeps S computed once for both dk and dv.  Under a causal mask the first key
 //          tiles see ~Tq/128 times the query rows of the last, so a key tile's (head,
 //          query tile) pairs may be cut into runs of one workgroup each, whose partial
 //          dk and dv a last kernel adds in run order.
@@ -281,8 +282,10 @@ constexpr int kBwdDkDv = 0, kBwdDk = 1, kBwdDv = 2;
 
 // dk/dv: a workgroup of NW waves owns 32 * NW keys of one (b, kv head); the query rows of
 // every head of the group stream through LDS in double-buffered tiles of BQ rows (q, w and
-// the row constants).  PART selects dk and dv, dk only, or dv only.
-template <int D, int BQ, int NW, int OCC, bool CAUSAL, int PART>
+// the row constants).  PART selects dk and dv, dk only, or dv only.  VLDS: the V operand
+// of G comes from the workgroup's V rows held in LDS for the whole kernel instead of
+// from registers.
+template <int D, int BQ, int NW, int OCC, bool CAUSAL, int PART, bool VLDS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_bwd_dkdv_mfma_kernel(
     const BwdMfmaParams p) {
   constexpr bool DK = PART != kBwdDv;
@@ -300,6 +303,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   __shared__ __attribute__((aligned(1024))) __bf16 w_buf1[BQ * D];
   __shared__ __attribute__((aligned(1024))) f32x4 r_buf0[64];
   __shared__ __attribute__((aligned(1024))) f32x4 r_buf1[64];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_rows[VLDS ? BK * D : 8];
+  static_assert(!VLDS || PART == kBwdDkDv || PART == kBwdDk, "only G reads V");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   for (int ks = 0; ks < KS; ++ks) {
     if (live) {
       kf[ks] = *(const bf16x8*)(p.k + kr * D + ks * 16 + 8 * half);
-      if constexpr (DK) vf[ks] = *(const bf16x8*)(p.v + kr * D + ks * 16 + 8 * half);
+      if constexpr (DK && !VLDS) vf[ks] = *(const bf16x8*)(p.v + kr * D + ks * 16 + 8 * half);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (__bf16)0.0f;
@@ -342,19 +347,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   const int q_x = half ^ chunk_swizzle<D>(col);
   const uint32_t q_base = (uint32_t)(col * D * 2 + 16 * (q_x & 1));
   const uint32_t q_xor = (uint32_t)(32 * (q_x >> 1));
+  // the wave's 32 V rows in the swizzled LDS image: row wave * 32 + col has the swizzle of
+  // row col (it repeats every 16 rows), so the row reads of the Q tile apply unchanged
+  const uint32_t v_wave = (uint32_t)(wave * 32 * D * 2);
+  if constexpr (VLDS) {
+    // rows at or past Tk lie outside the buffer range and read as zero; the first
+    // publish_tiles() of the loop below waits for these loads
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.v + (size_t)bk * Tk * D), (short)0, (uint32_t)((size_t)Tk * D * 2), 0x00020000);
+    load_tile<D, BK, NW>(vrs, key0, voff, v_rows, wave);
+  }
   const int gi = lane & 15;
   const int g = lane >> 4;
-  int t_off[2][DM];
+  // byte offsets of the transpose reads for d block 0; d block dm reads at t_byte ^ (64 dm):
+  // its logical chunk 4 dm + c0 (c0 < 4) enters the swizzled chunk only through bits 2-3,
+  // which sit at byte bits 6-7, and no other term of the offset (row * 2 D included) uses
+  // those bits for dm < D / 32
+  uint32_t t_byte[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int row = 8 * r + 4 * half + (gi >> 2);
     const int sw = chunk_swizzle<D>(row);
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
-      const int lchunk = 4 * dm + 2 * (g & 1) + ((gi & 3) >> 1);
-      t_off[r][dm] = row * D + ((lchunk ^ sw) << 3) + 4 * (gi & 1);
-    }
+    const int lchunk = 2 * (g & 1) + ((gi & 3) >> 1);
+    t_byte[r] = (uint32_t)(2 * (row * D + ((lchunk ^ sw) << 3) + 4 * (gi & 1)));
   }
+  auto tr_read = [&](const __bf16* tile, int kst, int dm) __attribute__((always_inline)) {
+    const char* base = (const char*)tile + kst * 16 * D * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(base + (t_byte[0] ^ (64u * dm))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(base + (t_byte[1] ^ (64u * dm))));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   f32x16 dk[DM], dv[DM];
 #pragma unroll
@@ -408,7 +432,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[mb], 0, 0, 0);
           if constexpr (DK) {
             const bf16x8 aw = *(const bf16x8*)((const char*)wt + o);
-            gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vf[ks], gg[mb], 0, 0, 0);
+            bf16x8 bv;
+            if constexpr (VLDS)
+              bv = *(const bf16x8*)((const char*)v_rows + v_wave + (q_base + ((32u * ks) ^ q_xor)));
+            else
+              bv = vf[ks];
+            gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bv, gg[mb], 0, 0, 0);
           }
         }
       // causal: key j is visible to row i iff j <= i + off; only tiles whose first rows
@@ -445,22 +474,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
       for (int kst = 0; kst < PS; ++kst)
 #pragma unroll
         for (int dm = 0; dm < DM; ++dm) {
-          if constexpr (DK) {
-            const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(qt + t_off[0][dm] + kst * 16 * D));
-            const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(qt + t_off[1][dm] + kst * 16 * D));
-            const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-            dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kst], dk[dm], 0, 0, 0);
-          }
-          if constexpr (DV) {
-            const s16x4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(wt + t_off[0][dm] + kst * 16 * D));
-            const s16x4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(wt + t_off[1][dm] + kst * 16 * D));
-            const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(wlo, whi, 0, 1, 2, 3, 4, 5, 6, 7));
-            dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, pf[kst], dv[dm], 0, 0, 0);
-          }
+          if constexpr (DK) dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt, kst, dm), dsf[kst], dk[dm], 0, 0, 0);
+          if constexpr (DV) dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(wt, kst, dm), pf[kst], dv[dm], 0, 0, 0);
         }
     };
 

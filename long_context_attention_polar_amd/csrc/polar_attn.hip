@@ -535,19 +535,11 @@ polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdM
   mp.n_kt = (mp.Tk + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
   const long long kblocks = (long long)mp.n_kt * mp.B * mp.Hkv * mp.n_split;
   if (kblocks > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-  // d = 64: dk and dv in one kernel with 32-row query tiles; d = 128: a dk kernel with
-  // 32-row tiles and a dv kernel with 64-row tiles; all at 2 waves per SIMD
+  // dk and dv in one kernel with 32-row query tiles at 2 waves per SIMD; at d = 128 the V
+  // operand of G is read from the workgroup's V rows in LDS
   const dim3 grid((unsigned)kblocks), block(kBwdWaves * 64);
-  if constexpr (D == 64) {
-    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv>, grid, block, mp,
-                stream);
-  } else {
-    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDk>, grid, block, mp,
-                stream);
-    if (st != POLAR_OK) return st;
-    st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 64, kBwdWaves, 2, CAUSAL, polar::kBwdDv>, grid, block, mp,
-                stream);
-  }
+  st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv, D == 128>, grid,
+              block, mp, stream);
   if (st != POLAR_OK || mp.n_split == 1) return st;
   mp.part_n4 = (long long)mp.B * mp.Hkv * mp.Tk * D / 4;
   const long long blocks = std::min((2 * mp.part_n4 + 255) / 256, 8192ll);
