@@ -70,8 +70,7 @@ KERNEL_SOURCES = {
     "merge_b64_h8_d128": (["decode.h"], "polar_merge_kernel"),
     "paged_gqa_decode_b64_h32_kv8_tk65536_d128": (["decode_group.h", "decode.h"], "polar_decode_group_kernel"),
     "bwd_dq_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dq_mfma_kernel"),
-    "bwd_dk_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
-    "bwd_dv_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
+    "bwd_dkdv_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),
     "bwd_split_sum_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_split_sum_kernel"),
 }
 
@@ -525,7 +524,7 @@ def main():
                              "note": "32 query heads share 8 KV heads; K and V are read once per group"},
         "backward": {"bound": "mfma", "achieved": res[BWD]["tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": res[BWD]["frac_bf16_peak"], "ms": res[BWD]["ms_avg"],
-                     "traffic_dk": measured_traffic("bwd_dk_b1_h16_kv4_t16384_d128"),
+                     "traffic_dkdv": measured_traffic("bwd_dkdv_b1_h16_kv4_t16384_d128"),
                      "note": "bf16 matrix-core path: forward statistics, row constants, dq, dk, dv; "
                              "10 d algorithmic flops per causal pair"},
         "chunked_prefill": {"bound": "mfma", "achieved": res[CHUNKED]["tflops"], "peak": PEAK_BF16_TFLOPS,

@@ -277,19 +277,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           f32x4{dq[dm][4 * i], dq[dm][4 * i + 1], dq[dm][4 * i + 2], dq[dm][4 * i + 3]};
 }
 
-// Which gradients a key-side kernel accumulates.
-constexpr int kBwdDkDv = 0, kBwdDk = 1, kBwdDv = 2;
-
 // dk/dv: a workgroup of NW waves owns 32 * NW keys of one (b, kv head); the query rows of
 // every head of the group stream through LDS in double-buffered tiles of BQ rows (q, w and
-// the row constants).  PART selects dk and dv, dk only, or dv only.  VLDS: the V operand
-// of G comes from the workgroup's V rows held in LDS for the whole kernel instead of
-// from registers.
-template <int D, int BQ, int NW, int OCC, bool CAUSAL, int PART, bool VLDS = false>
+// the row constants).  VLDS: the V operand of G comes from the workgroup's V rows held in
+// LDS for the whole kernel instead of from registers.
+template <int D, int BQ, int NW, int OCC, bool CAUSAL, bool VLDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void polar_bwd_dkdv_mfma_kernel(
     const BwdMfmaParams p) {
-  constexpr bool DK = PART != kBwdDv;
-  constexpr bool DV = PART != kBwdDk;
   constexpr int BK = NW * 32;
   constexpr int MB = BQ / 32;
   constexpr int KS = D / 16;
@@ -304,7 +298,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   __shared__ __attribute__((aligned(1024))) f32x4 r_buf0[64];
   __shared__ __attribute__((aligned(1024))) f32x4 r_buf1[64];
   __shared__ __attribute__((aligned(1024))) __bf16 v_rows[VLDS ? BK * D : 8];
-  static_assert(!VLDS || PART == kBwdDkDv || PART == kBwdDk, "only G reads V");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -336,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   for (int ks = 0; ks < KS; ++ks) {
     if (live) {
       kf[ks] = *(const bf16x8*)(p.k + kr * D + ks * 16 + 8 * half);
-      if constexpr (DK && !VLDS) vf[ks] = *(const bf16x8*)(p.v + kr * D + ks * 16 + 8 * half);
+      if constexpr (!VLDS) vf[ks] = *(const bf16x8*)(p.v + kr * D + ks * 16 + 8 * half);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (__bf16)0.0f;
@@ -430,15 +423,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
           const uint32_t o = (q_base + ((32u * ks) ^ q_xor)) + mb * 32 * D * 2;
           const bf16x8 aq = *(const bf16x8*)((const char*)qt + o);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[mb], 0, 0, 0);
-          if constexpr (DK) {
-            const bf16x8 aw = *(const bf16x8*)((const char*)wt + o);
-            bf16x8 bv;
-            if constexpr (VLDS)
-              bv = *(const bf16x8*)((const char*)v_rows + v_wave + (q_base + ((32u * ks) ^ q_xor)));
-            else
-              bv = vf[ks];
-            gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bv, gg[mb], 0, 0, 0);
-          }
+          const bf16x8 aw = *(const bf16x8*)((const char*)wt + o);
+          bf16x8 bv;
+          if constexpr (VLDS)
+            bv = *(const bf16x8*)((const char*)v_rows + v_wave + (q_base + ((32u * ks) ^ q_xor)));
+          else
+            bv = vf[ks];
+          gg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bv, gg[mb], 0, 0, 0);
         }
       // causal: key j is visible to row i iff j <= i + off; only tiles whose first rows
       // precede the wave's last key need the mask, applied in place in a pass of its own so
@@ -463,19 +454,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             const f32x4 rv = rt[r];
             const float x = s[mb][4 * i + j];
             const float pv = fast_exp2(fmaf(rv[1], x, -rv[0]));
-            if constexpr (DV) pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
-            if constexpr (DK) {
-              const float dsv = pv * fmaf(rv[3], pv, fmaf(rv[1] * kLn2, gg[mb][4 * i + j], rv[2]));
-              dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
-            }
+            pf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)pv;
+            const float dsv = pv * fmaf(rv[3], pv, fmaf(rv[1] * kLn2, gg[mb][4 * i + j], rv[2]));
+            dsf[mb * 2 + (i >> 1)][(i & 1) * 4 + j] = (__bf16)dsv;
           }
       // dK^T += Q^T dS, dV^T += W^T P
 #pragma unroll
       for (int kst = 0; kst < PS; ++kst)
 #pragma unroll
         for (int dm = 0; dm < DM; ++dm) {
-          if constexpr (DK) dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt, kst, dm), dsf[kst], dk[dm], 0, 0, 0);
-          if constexpr (DV) dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(wt, kst, dm), pf[kst], dv[dm], 0, 0, 0);
+          dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt, kst, dm), dsf[kst], dk[dm], 0, 0, 0);
+          dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(wt, kst, dm), pf[kst], dv[dm], 0, 0, 0);
         }
     };
 
@@ -503,12 +492,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (DK)
-        *(f32x4*)(ok + dm * 32 + 8 * i + 4 * half) =
-            f32x4{dk[dm][4 * i], dk[dm][4 * i + 1], dk[dm][4 * i + 2], dk[dm][4 * i + 3]};
-      if constexpr (DV)
-        *(f32x4*)(ov + dm * 32 + 8 * i + 4 * half) =
-            f32x4{dv[dm][4 * i], dv[dm][4 * i + 1], dv[dm][4 * i + 2], dv[dm][4 * i + 3]};
+      *(f32x4*)(ok + dm * 32 + 8 * i + 4 * half) =
+          f32x4{dk[dm][4 * i], dk[dm][4 * i + 1], dk[dm][4 * i + 2], dk[dm][4 * i + 3]};
+      *(f32x4*)(ov + dm * 32 + 8 * i + 4 * half) =
+          f32x4{dv[dm][4 * i], dv[dm][4 * i + 1], dv[dm][4 * i + 2], dv[dm][4 * i + 3]};
     }
 }
 

@@ -538,7 +538,7 @@ polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdM
   // dk and dv in one kernel with 32-row query tiles at 2 waves per SIMD; at d = 128 the V
   // operand of G is read from the workgroup's V rows in LDS
   const dim3 grid((unsigned)kblocks), block(kBwdWaves * 64);
-  st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, polar::kBwdDkDv, D == 128>, grid,
+  st = launch(polar::polar_bwd_dkdv_mfma_kernel<D, 32, kBwdWaves, 2, CAUSAL, D == 128>, grid,
               block, mp, stream);
   if (st != POLAR_OK || mp.n_split == 1) return st;
   mp.part_n4 = (long long)mp.B * mp.Hkv * mp.Tk * D / 4;
