@@ -19,10 +19,10 @@
 //          in registers at d = 64; at d = 128 the four accumulators and both K and V
 //          fragments would not fit one wave's share of two waves per SIMD, so the
 //          workgroup's 128 V rows are loaded once into LDS and G reads its V operand
-//          from there, which keeps S computed once for both dk and dv.  Under a causal mask the first key
-//          tiles see ~Tq/128 times the query rows of the last, so a key tile's (head,
-//          query tile) pairs may be cut into runs of one workgroup each, whose partial
-//          dk and dv a last kernel adds in run order.
+//          from there, which keeps S computed once for both dk and dv.  Under a causal
+//          mask the first key tiles see ~Tq/128 times the query rows of the last, so a
+//          key tile's (head, query tile) pairs may be cut into runs of one workgroup
+//          each, whose partial dk and dv a last kernel adds in run order.
 // P, dS and w enter the products as bf16 (round to nearest even); every sum is fp32.
 #pragma once
 
