@@ -18,6 +18,15 @@
 // The arithmetic of a query does not depend on whether the cache is paged (only the row
 // address differs), so paged and contiguous runs give bitwise-equal partials.
 //
+// At head_dim 128 (16 lanes per key) with several query heads the lanes of a key split
+// the heads between them: the row sum of the G partial dots leaves each lane with one
+// head's full dot (split_row_sum), so the scores, the running maximum, the exponentials
+// and the sums are formed once per head instead of once per lane and head; each head's
+// weight and correction factor then reach the lanes of its row by a DPP broadcast for
+// the value products, which every lane keeps for all G heads over its 8 dims.  The K and
+// V rows of the next iteration are loaded into a second register set while the current
+// one is computed.
+//
 // Reading variants: a sliding window keeps the last `window` keys of each sequence (the
 // splits cover [len - window, len)); a per-key floor reduces each weight against the
 // floor of the query's visible count (the template flag KF, so the default kernels carry
@@ -29,6 +38,65 @@
 namespace polar {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// One reduction step of the head-split row sum: the lane keeps the first N/2 of its N live
+// slots and adds to slot j the partner's slot N-1-j (N <= 1: a plain step on slot 0).
+template <int CTRL, int N, int G>
+__device__ __forceinline__ void split_step(float (&r)[G]) {
+  if constexpr (N > 1) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) r[j] += dpp_move<CTRL>(r[N - 1 - j]);
+  } else {
+    r[0] += dpp_move<CTRL>(r[0]);
+  }
+}
+
+// Sum over a row of 16 lanes (one key of a head_dim 128 row, 8 dims per lane) of the
+// partial dots of G query heads, split so that each lane ends with one head's full dot.
+// Slot j of lane l holds head j ^ M with M = (l mod 16) >> (4 - log2 G); the four steps
+// pair lane i with 15 - i (row mirror: flips every lane bit), 7 - i in its half (half
+// mirror), i ^ 2 and i ^ 1.  A pairing step that flips the lane bit that picks the top
+// live head bit halves the live slots: slot j takes the partner's slot N-1-j, which holds
+// the same head, because the partner's M differs from this lane's in exactly the live
+// bits the step flips.  After the steps slot 0 holds the dot of head M summed over all 16
+// lanes, in the same order in every lane that holds that head (each add is commutative
+// across the pair).
+template <int G>
+__device__ __forceinline__ float split_row_sum(float (&r)[G]) {
+  split_step<0x140, G, G>(r);      // row_mirror
+  split_step<0x141, G / 2, G>(r);  // row_half_mirror
+  split_step<0x4E, G / 4, G>(r);   // quad_perm [2,3,0,1]
+  split_step<0xB1, G / 8, G>(r);   // quad_perm [1,0,3,2]
+  return r[0];
+}
+
+// Broadcast of lane n of each row of 16 (row_newbcast), n a compile-time value after
+// unrolling.
+__device__ __forceinline__ float row_bcast(float x, int n) {
+  switch (n) {
+    case 0: return dpp_move<0x150>(x);
+    case 1: return dpp_move<0x151>(x);
+    case 2: return dpp_move<0x152>(x);
+    case 3: return dpp_move<0x153>(x);
+    case 4: return dpp_move<0x154>(x);
+    case 5: return dpp_move<0x155>(x);
+    case 6: return dpp_move<0x156>(x);
+    case 7: return dpp_move<0x157>(x);
+    case 8: return dpp_move<0x158>(x);
+    case 9: return dpp_move<0x159>(x);
+    case 10: return dpp_move<0x15A>(x);
+    case 11: return dpp_move<0x15B>(x);
+    case 12: return dpp_move<0x15C>(x);
+    case 13: return dpp_move<0x15D>(x);
+    case 14: return dpp_move<0x15E>(x);
+    default: return dpp_move<0x15F>(x);
+  }
+}
 
 struct GroupDecodeParams {
   const void* q;           // [B, H, D] bf16
@@ -47,10 +115,11 @@ struct GroupDecodeParams {
   HeadParams hp;
 };
 
-// Four query heads and no per-key floor: held to 128 registers (4 waves per SIMD), which
-// they fit without spills; the other instances keep the compiler's choice.
+// Four query heads and no per-key floor: held to 168 registers (3 waves per SIMD), which
+// they fit without spills (at 128 registers the two register sets spill); the other
+// instances keep the compiler's choice.
 template <int D, int G, int NW, int UNROLL, bool PAGED, int KF = POLAR_KEY_FLOOR_NULL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(G == 4 && KF == POLAR_KEY_FLOOR_NULL ? 4
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(G == 4 && KF == POLAR_KEY_FLOOR_NULL ? 3
                                                                                                                : 1))) void
 polar_decode_group_kernel(const GroupDecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key (8 dims each)
@@ -67,6 +136,13 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
   const int sub = lane / LPK;          // key slot inside the wave
   const int dch = lane % LPK;          // 8-dim chunk of this lane
   const int slot = wave * KPW + sub;
+  // head_dim 128 with several query heads: the 16 lanes of a key split the heads between
+  // them for the sum of the dot and for the weights (each lane one head, split_row_sum),
+  // and each head's weight is then broadcast from its lanes to the row for P V
+  constexpr bool kSplit = D == 128 && G > 1;
+  constexpr int kLog2G = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 0;
+  constexpr int kLanesPerHead = 16 >> kLog2G;
+  const int hm = kSplit ? dch >> (4 - kLog2G) : 0;  // the head this lane finishes (split form)
 
   const int s = blockIdx.x;
   const int hk = blockIdx.y / p.chunks;
@@ -80,15 +156,17 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
   const int n = max(len - start, 1);
 
   // One query per sequence; it sees every cached key of its sequence (or the last
-  // `window` of them), n = len - start (never a per-split count).
+  // `window` of them), n = len - start (never a per-split count).  Slot g holds query
+  // head g, or head g ^ hm in the split form.
   uint32_t qw[G][4];
   float c[G], f2[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const u32x4 w = *(const u32x4*)((const __bf16*)p.q + ((size_t)b * p.H + h0 + g) * D + dch * 8);
+    const int hg = h0 + (kSplit ? g ^ hm : g);
+    const u32x4 w = *(const u32x4*)((const __bf16*)p.q + ((size_t)b * p.H + hg) * D + dch * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qw[g][e] = w[e];
-    const int hpi = (h0 + g) * p.hp_stride;
+    const int hpi = hg * p.hp_stride;
     const float lam = row_temperature(p.hp, hpi, n);
     c[g] = logit_scale(lam, p.scale);
     f2[g] = 0.0f;
@@ -123,70 +201,123 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   }
 
-  // paged: the block-table entries of an iteration's keys are loaded one iteration ahead,
-  // so the K/V loads never wait on a table read
-  int32_t next_blk[UNROLL];
+  // The K and V rows of an iteration (UNROLL keys per slot) are loaded into one of two
+  // register sets while the keys of the other set are computed, so one iteration's loads
+  // are in flight during the previous iteration's arithmetic.  Paged: the block-table
+  // entries of a set are loaded before the set itself is issued.
+  constexpr int STEP = NSLOT * UNROLL;
+  struct Rows {
+    u32x4 k[UNROLL], v[UNROLL];
+    bool ok[UNROLL];
+  };
+  int32_t tbl[UNROLL];
   auto table_entries = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int key = base + slot + u * NSLOT;
-      next_blk[u] = key < hi ? trow[key >> p.bs_log2] : 0;
+      tbl[u] = key < hi ? trow[key >> p.bs_log2] : 0;
     }
   };
-  if constexpr (PAGED) table_entries(lo);
-
-  for (int base = lo; base < hi; base += NSLOT * UNROLL) {
-    u32x4 kr[UNROLL], vr[UNROLL];
-    bool ok[UNROLL];
-    int32_t blk[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) blk[u] = next_blk[u];
+  auto issue = [&](int base, Rows& r) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int key = base + slot + u * NSLOT;
-      ok[u] = key < hi;
+      r.ok[u] = key < hi;
       size_t row = 0;
       if constexpr (PAGED) {
-        ok[u] = ok[u] && (uint32_t)blk[u] < (uint32_t)p.num_blocks;
-        row = (((size_t)(uint32_t)blk[u] << p.bs_log2) + (key & bs_mask)) * p.Hkv + hk;
+        r.ok[u] = r.ok[u] && (uint32_t)tbl[u] < (uint32_t)p.num_blocks;
+        row = (((size_t)(uint32_t)tbl[u] << p.bs_log2) + (key & bs_mask)) * p.Hkv + hk;
       } else {
         row = (size_t)key;
       }
-      if (ok[u]) {
+      if (r.ok[u]) {
         const size_t off = (PAGED ? row * D : cont_off + row * D) + dch * 8;
-        kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));  // read once
-        vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
+        r.k[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));  // read once
+        r.v[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
       } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
+        r.k[u] = u32x4{0, 0, 0, 0};
+        r.v[u] = u32x4{0, 0, 0, 0};
       }
     }
-    if constexpr (PAGED) table_entries(base + NSLOT * UNROLL);
+  };
+  auto compute = [&](const Rows& r) __attribute__((always_inline)) {
     float vf[UNROLL][8];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[u][2 * e] = bf16_lo(vr[u][e]);
-        vf[u][2 * e + 1] = bf16_hi(vr[u][e]);
+        vf[u][2 * e] = bf16_lo(r.v[u][e]);
+        vf[u][2 * e + 1] = bf16_hi(r.v[u][e]);
       }
+    if constexpr (kSplit) {
+      // this lane's head (slot 0): scores, running maximum, weights and sums
+      float x[UNROLL];
+      float xmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float part[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float t = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t qe = qw[g][e], ke = r.k[u][e];
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qe), __builtin_bit_cast(bf16x2_t, ke), t,
+                                                false);
+          }
+          part[g] = t;
+        }
+        const float dot = split_row_sum<G>(part);
+        x[u] = r.ok[u] ? c[0] * dot : -INFINITY;
+        xmax = fmaxf(xmax, x[u]);
+      }
+      const float m_new = fmaxf(m[0], xmax);
+      const float alpha = fast_exp2(m[0] - m_new);
+      s1[0] *= alpha;
+      s2[0] *= alpha * alpha;  // squared correction factor
+      m[0] = m_new;
+      const float phi = KF == POLAR_KEY_FLOOR_SOFT ? fast_exp2(f2[0] - m[0]) : 0.0f;
+      float pw[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float pv = fast_exp2(x[u] - m[0]);
+        if constexpr (KF == POLAR_KEY_FLOOR_SOFT) pv = fmaxf(pv - phi, 0.0f);
+        if constexpr (KF == POLAR_KEY_FLOOR_GATE) pv = x[u] > f2[0] ? pv : 0.0f;
+        s1[0] += pv;
+        s2[0] = fmaf(pv, pv, s2[0]);
+        pw[u] = pv;
+      }
+      // every head's correction factor and weights, from the first lane holding that head
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float ag = row_bcast(alpha, g * kLanesPerHead);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const float pg = row_bcast(pw[u], g * kLanesPerHead);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pg, vf[u][e], acc[g][e]);
+        }
+      }
+    } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float x[UNROLL];
       float xmax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        float r = 0.0f;
+        float dt = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // copy the elements out first: a bit cast applied to a vector subscript reads
           // element 0 whatever the index (seen with this compiler)
-          const uint32_t qe = qw[g][e], ke = kr[u][e];
-          r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qe), __builtin_bit_cast(bf16x2_t, ke), r,
-                                              false);
+          const uint32_t qe = qw[g][e], ke = r.k[u][e];
+          dt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qe), __builtin_bit_cast(bf16x2_t, ke), dt,
+                                               false);
         }
-        r = group_sum<LPK>(r);
-        x[u] = ok[u] ? c[g] * r : -INFINITY;
+        dt = group_sum<LPK>(dt);
+        x[u] = r.ok[u] ? c[g] * dt : -INFINITY;
         xmax = fmaxf(xmax, x[u]);
       }
       const float m_new = fmaxf(m[g], xmax);
@@ -209,15 +340,30 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
         for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pv, vf[u][e], acc[g][e]);
       }
     }
+    }
+  };
+
+  Rows ra, rb;
+  if constexpr (PAGED) table_entries(lo);
+  issue(lo, ra);
+  if constexpr (PAGED) table_entries(lo + STEP);
+  for (int base = lo; base < hi; base += 2 * STEP) {
+    issue(base + STEP, rb);
+    if constexpr (PAGED) table_entries(base + 2 * STEP);
+    compute(ra);
+    if (base + STEP >= hi) break;
+    issue(base + 2 * STEP, ra);
+    if constexpr (PAGED) table_entries(base + 3 * STEP);
+    compute(rb);
   }
 
   // ---- per query head: combine the slots of the workgroup into one partial row
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (dch == 0) {
-      slot_m[slot] = m[g];
-      slot_s1[slot] = s1[g];
-      slot_s2[slot] = s2[g];
+    if (kSplit ? dch == g * kLanesPerHead : dch == 0) {
+      slot_m[slot] = m[kSplit ? 0 : g];
+      slot_s1[slot] = s1[kSplit ? 0 : g];
+      slot_s2[slot] = s2[kSplit ? 0 : g];
     }
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {

@@ -118,10 +118,13 @@ def test_paged_equals_contiguous_bitwise(Tk):
         assert_parity(pag, ref, "bf16", label=f"paged Tk={Tk} S={pag['splits']}")
 
 
-def test_grouped_matches_per_head_reads():
-    """GQA (4 query heads per KV head) against the same caches repeated for every query
-    head (plain multi-head layout): equal up to fp32 summation order."""
-    B, H, Hkv, Tk, d = 2, 8, 2, 900, 64
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H", [4, 8, 16])
+def test_grouped_matches_per_head_reads(d, H):
+    """GQA (2, 4 or 8 query heads per KV head) against the same caches repeated for every
+    query head (plain multi-head layout): equal up to fp32 summation order.  At head_dim
+    128 the grouped kernel splits the heads over the lanes of a key for the dot's sum."""
+    B, Hkv, Tk = 2, 2, 900
     q, k, v, _ = pin.random_qkv(B, H, Hkv, 1, Tk, d, torch.bfloat16, 91)
     rep_k = k.repeat_interleave(H // Hkv, dim=1).contiguous()
     rep_v = v.repeat_interleave(H // Hkv, dim=1).contiguous()
