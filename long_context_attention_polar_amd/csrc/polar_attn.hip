@@ -223,10 +223,15 @@ polar_status launch_bf16_kf(const FwdParams& fp, unsigned blocks, void* stream) 
     // A causal grid the chip holds in one round lasts as long as its heaviest query tile;
     // at d = 64 such grids take query tiles of half the rows (one 32-row block per wave,
     // 160 registers, so three waves per SIMD), which the heaviest-first order spreads over
-    // more resident slots.  Larger grids, and every non-causal one (equal tiles), keep two
-    // blocks per wave, which share each K and V operand read between two MFMAs.
+    // more resident slots -- when the tiles' key counts differ widely (fewer keys before
+    // the first row than rows), or when the half-height grid itself fits one round.  A
+    // chunk of rows after a long prefix has tiles of nearly equal work, where a second
+    // round of half-height tiles costs more than it saves.  Larger grids, and every
+    // non-causal one (equal tiles), keep two blocks per wave, which share each K and V
+    // operand read between two MFMAs.
     if constexpr (D == 64 && NB == 2 && CAUSAL) {
-      if (blocks <= (unsigned)kResidentWorkgroups<OCC>()) {
+      if (blocks <= (unsigned)kResidentWorkgroups<OCC>() &&
+          (fp.Tk - fp.Tq < fp.Tq || 2 * blocks <= (unsigned)kResidentWorkgroups<kBf16Occ_d64_one_round>())) {
         FwdParams f1 = fp;
         constexpr int BM1 = kBf16Waves * 32;
         f1.n_qt = (fp.Tq + BM1 - 1) / BM1;
