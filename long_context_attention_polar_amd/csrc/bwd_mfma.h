@@ -58,37 +58,40 @@ struct BwdMfmaParams {
   HeadParams hp;
 };
 
-// One wave per query row: w = (g_u - u (u . g_u)) / ||acc|| as bf16, and the row constants.
+// Sixteen lanes per query row (four rows per wave): w = (g_u - u (u . g_u)) / ||acc|| as
+// bf16, and the row constants, which the row's first lane forms.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void polar_bwd_prep_kernel(const BwdMfmaParams p) {
-  constexpr int DPL = D / 64;  // dims per lane
-  const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * H + h) * Tq + i
+  constexpr int DPL = D / 16;  // dims per lane: lane c of a row holds dims e * 16 + c
+  const int c = threadIdx.x & 15;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b * H + h) * Tq + i
   const size_t rows = (size_t)p.B * p.H * p.Tq;
-  if (row >= rows) return;  // whole waves leave together
-  const int i = (int)(row % p.Tq);
-  const int h = (int)((row / p.Tq) % p.H);
-  const float* pr = p.part + row * (D + 3);
+  const bool ok = row < rows;  // a row past the end still takes part in the lane sums
+  const size_t rr = ok ? row : 0;
+  const float* pr = p.part + rr * (D + 3);
   float acc[DPL], gu[DPL];
   float nn = 0.0f;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
-    acc[e] = pr[3 + lane + 64 * e];
-    gu[e] = p.g_dir ? p.g_dir[row * D + lane + 64 * e] : 0.0f;
+    acc[e] = ok ? pr[3 + 16 * e + c] : 0.0f;
+    gu[e] = ok && p.g_dir ? p.g_dir[rr * D + 16 * e + c] : 0.0f;
     nn = fmaf(acc[e], acc[e], nn);
   }
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) nn += __shfl_xor(nn, sh, 64);
+  for (int sh = 8; sh >= 1; sh >>= 1) nn += __shfl_xor(nn, sh, 16);
   const float a = sqrtf(nn);
   const float inv_a = a > 0.0f ? 1.0f / a : 0.0f;  // acc == 0: zero direction, w = 0
   float ug = 0.0f;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) ug = fmaf(acc[e] * inv_a, gu[e], ug);
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) ug += __shfl_xor(ug, sh, 64);
+  for (int sh = 8; sh >= 1; sh >>= 1) ug += __shfl_xor(ug, sh, 16);
+  if (!ok) return;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) p.W[row * D + lane + 64 * e] = (__bf16)((gu[e] - acc[e] * inv_a * ug) * inv_a);
-  if (lane == 0) {
+  for (int e = 0; e < DPL; ++e) p.W[row * D + 16 * e + c] = (__bf16)((gu[e] - acc[e] * inv_a * ug) * inv_a);
+  if (c == 0) {
+    const int i = (int)(row % p.Tq);
+    const int h = (int)((row / p.Tq) % p.H);
     const int hpi = h * p.hp_stride;
     const int n = visible_keys(i, p.Tq, p.Tk, CAUSAL);
     const float lam = row_temperature(p.hp, hpi, n);
@@ -98,9 +101,9 @@ __global__ __launch_bounds__(256) void polar_bwd_prep_kernel(const BwdMfmaParams
                   p.g_conf ? p.g_conf[row] : 0.0f, p.g_count ? p.g_count[row] : 0.0f, c1, c2);
     // the products take dS scaled by cl = lam scale, the factor dq and dk carry:
     // cl dS = p (cl c1 + 2 cl c2 p + cl <w, v>)
-    const float c = logit_scale(lam, p.scale);
-    const float cl = c * kLn2;
-    p.R[row] = f32x4{m_nat * kLog2e, c, cl * c1, 2.0f * cl * c2};
+    const float cs = logit_scale(lam, p.scale);
+    const float cl = cs * kLn2;
+    p.R[row] = f32x4{m_nat * kLog2e, cs, cl * c1, 2.0f * cl * c2};
   }
 }
 

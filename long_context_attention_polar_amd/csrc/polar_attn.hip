@@ -526,8 +526,8 @@ polar_status launch_bwd_mfma(const polar_problem* pr, FwdParams& fp, polar::BwdM
       if (st != POLAR_OK) return st;
     }
     const long long rows = (long long)mp.B * mp.H * mp.Tq;
-    if ((rows + 3) / 4 > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-    st = launch(polar::polar_bwd_prep_kernel<D, CAUSAL>, dim3((unsigned)((rows + 3) / 4)), dim3(256), mp, stream);
+    if ((rows + 15) / 16 > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
+    st = launch(polar::polar_bwd_prep_kernel<D, CAUSAL>, dim3((unsigned)((rows + 15) / 16)), dim3(256), mp, stream);
     if (st != POLAR_OK) return st;
     mp.n_qt = (mp.Tq + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
     const long long qblocks = (long long)mp.n_qt * mp.B * mp.H;
