@@ -18,12 +18,12 @@
 // The arithmetic of a query does not depend on whether the cache is paged (only the row
 // address differs), so paged and contiguous runs give bitwise-equal partials.
 //
-// At head_dim 128 (16 lanes per key) with several query heads the lanes of a key split
-// the heads between them: the row sum of the G partial dots leaves each lane with one
-// head's full dot (split_row_sum), so the scores, the running maximum, the exponentials
-// and the sums are formed once per head instead of once per lane and head; each head's
-// weight and correction factor then reach the lanes of its row by a DPP broadcast for
-// the value products, which every lane keeps for all G heads over its 8 dims.  The K and
+// With several query heads the lanes of a key (16 at head_dim 128, 8 at 64) split the
+// heads between them: the sum of the G partial dots leaves each lane with one head's
+// full dot (split_row_sum), so the scores, the running maximum, the exponentials and
+// the sums are formed once per head instead of once per lane and head; each head's
+// weight and correction factor then reach the key's lanes by DPP broadcasts for the
+// value products, which every lane keeps for all G heads over its 8 dims.  The K and
 // V rows of the next iteration are loaded into a second register set while the current
 // one is computed.
 //
@@ -45,33 +45,42 @@ __device__ __forceinline__ float dpp_move(float x) {
 }
 
 // One reduction step of the head-split row sum: the lane keeps the first N/2 of its N live
-// slots and adds to slot j the partner's slot N-1-j (N <= 1: a plain step on slot 0).
-template <int CTRL, int N, int G>
+// slots and adds to slot j the partner's slot holding the same head -- N-1-j when the
+// step's lane pairing flips every live head bit of M (a mirror), j + N/2 when it flips
+// only the top one (a single-bit exchange); N <= 1: a plain step on slot 0.
+template <int CTRL, bool MIRROR, int N, int G>
 __device__ __forceinline__ void split_step(float (&r)[G]) {
   if constexpr (N > 1) {
 #pragma unroll
-    for (int j = 0; j < N / 2; ++j) r[j] += dpp_move<CTRL>(r[N - 1 - j]);
+    for (int j = 0; j < N / 2; ++j) r[j] += dpp_move<CTRL>(r[MIRROR ? N - 1 - j : j + N / 2]);
   } else {
     r[0] += dpp_move<CTRL>(r[0]);
   }
 }
 
-// Sum over a row of 16 lanes (one key of a head_dim 128 row, 8 dims per lane) of the
-// partial dots of G query heads, split so that each lane ends with one head's full dot.
-// Slot j of lane l holds head j ^ M with M = (l mod 16) >> (4 - log2 G); the four steps
-// pair lane i with 15 - i (row mirror: flips every lane bit), 7 - i in its half (half
-// mirror), i ^ 2 and i ^ 1.  A pairing step that flips the lane bit that picks the top
-// live head bit halves the live slots: slot j takes the partner's slot N-1-j, which holds
-// the same head, because the partner's M differs from this lane's in exactly the live
-// bits the step flips.  After the steps slot 0 holds the dot of head M summed over all 16
-// lanes, in the same order in every lane that holds that head (each add is commutative
-// across the pair).
-template <int G>
+// Sum over the LPK lanes of one key (8 dims per lane: 16 lanes at head_dim 128, 8 at 64)
+// of the partial dots of G <= LPK query heads, split so that each lane ends with one head's
+// full dot.  Slot j of lane l holds head j ^ M with M = (l mod LPK) >> (log2 LPK - log2 G):
+// the top lane bits pick the head.  The steps pair lane i with 15 - i (row mirror: flips
+// every lane bit; LPK = 16 only), 7 - i in its half of 8 (half mirror: flips the three low
+// bits), i ^ 2 and i ^ 1.  A step whose flipped bits include the lane bit of the top live
+// head bit halves the live slots, and the partner's M differs from this lane's in exactly
+// the live head bits the step flips, which gives the partner slot that holds the same head
+// (split_step).  After the steps slot 0 holds the dot of head M summed over all LPK lanes,
+// in the same order in every lane that holds that head (each add is commutative across
+// the pair).
+template <int G, int LPK>
 __device__ __forceinline__ float split_row_sum(float (&r)[G]) {
-  split_step<0x140, G, G>(r);      // row_mirror
-  split_step<0x141, G / 2, G>(r);  // row_half_mirror
-  split_step<0x4E, G / 4, G>(r);   // quad_perm [2,3,0,1]
-  split_step<0xB1, G / 8, G>(r);   // quad_perm [1,0,3,2]
+  if constexpr (LPK == 16) {
+    split_step<0x140, true, G, G>(r);       // row_mirror
+    split_step<0x141, true, G / 2, G>(r);   // row_half_mirror
+    split_step<0x4E, false, G / 4, G>(r);   // quad_perm [2,3,0,1]
+    split_step<0xB1, false, G / 8, G>(r);   // quad_perm [1,0,3,2]
+  } else {
+    split_step<0x141, true, G, G>(r);       // row_half_mirror
+    split_step<0x4E, false, G / 2, G>(r);   // quad_perm [2,3,0,1]
+    split_step<0xB1, false, G / 4, G>(r);   // quad_perm [1,0,3,2]
+  }
   return r[0];
 }
 
@@ -95,6 +104,26 @@ __device__ __forceinline__ float row_bcast(float x, int n) {
     case 13: return dpp_move<0x15D>(x);
     case 14: return dpp_move<0x15E>(x);
     default: return dpp_move<0x15F>(x);
+  }
+}
+
+// Broadcast of lane n of each group of 8 lanes: row_newbcast from lane n into the low half
+// of each row of 16 (banks 0-1) and from lane 8 + n into its high half (banks 2-3).
+template <int N>
+__device__ __forceinline__ float half_row_bcast(float x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0x3, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(lo, __builtin_bit_cast(int, x), 0x158 + N, 0xF, 0xC, false));
+}
+__device__ __forceinline__ float group8_bcast(float x, int n) {
+  switch (n) {
+    case 0: return half_row_bcast<0>(x);
+    case 1: return half_row_bcast<1>(x);
+    case 2: return half_row_bcast<2>(x);
+    case 3: return half_row_bcast<3>(x);
+    case 4: return half_row_bcast<4>(x);
+    case 5: return half_row_bcast<5>(x);
+    case 6: return half_row_bcast<6>(x);
+    default: return half_row_bcast<7>(x);
   }
 }
 
@@ -136,13 +165,19 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
   const int sub = lane / LPK;          // key slot inside the wave
   const int dch = lane % LPK;          // 8-dim chunk of this lane
   const int slot = wave * KPW + sub;
-  // head_dim 128 with several query heads: the 16 lanes of a key split the heads between
-  // them for the sum of the dot and for the weights (each lane one head, split_row_sum),
-  // and each head's weight is then broadcast from its lanes to the row for P V
-  constexpr bool kSplit = D == 128 && G > 1;
+  // several query heads: the LPK lanes of a key split the heads between them for the sum
+  // of the dot and for the weights (each lane one head, split_row_sum), and each head's
+  // weight is then broadcast from its lanes to the key's lanes for P V.  Not for two heads
+  // over 8 lanes, where the two-move broadcasts cost about what the split saves.
+  constexpr bool kSplit = G > 1 && (LPK == 16 || G > 2);
   constexpr int kLog2G = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 0;
-  constexpr int kLanesPerHead = 16 >> kLog2G;
-  const int hm = kSplit ? dch >> (4 - kLog2G) : 0;  // the head this lane finishes (split form)
+  constexpr int kLog2L = LPK == 16 ? 4 : 3;
+  constexpr int kLanesPerHead = LPK >> kLog2G;
+  const int hm = kSplit ? dch >> (kLog2L - kLog2G) : 0;  // the head this lane finishes (split form)
+  auto head_bcast = [&](float x, int g) __attribute__((always_inline)) {
+    if constexpr (LPK == 16) return row_bcast(x, g * kLanesPerHead);
+    else return group8_bcast(x, g * kLanesPerHead);
+  };
 
   const int s = blockIdx.x;
   const int hk = blockIdx.y / p.chunks;
@@ -267,7 +302,7 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
           }
           part[g] = t;
         }
-        const float dot = split_row_sum<G>(part);
+        const float dot = split_row_sum<G, LPK>(part);
         x[u] = r.ok[u] ? c[0] * dot : -INFINITY;
         xmax = fmaxf(xmax, x[u]);
       }
@@ -290,12 +325,12 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
       // every head's correction factor and weights, from the first lane holding that head
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float ag = row_bcast(alpha, g * kLanesPerHead);
+        const float ag = head_bcast(alpha, g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const float pg = row_bcast(pw[u], g * kLanesPerHead);
+          const float pg = head_bcast(pw[u], g);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pg, vf[u][e], acc[g][e]);
         }
