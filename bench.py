@@ -256,11 +256,11 @@ def cpu_baseline(seconds):
             "_pairs": pairs, "_seconds": dt}
 
 
-def oracle_per_config(c3_sample, gpu_ms, decode_inputs):
+def oracle_per_config(prefill16k_sample, gpu_ms, decode_inputs):
     """The fp64 oracle timed on every configuration: whole for the two small ones, on a
     bounded sample for the others, scaled to the whole configuration by its (query, key)
     pairs (the oracle's work is proportional to them: one row block costs its rows times
-    its visible keys).  `c3_sample` is the 16K prefill sample of cpu_baseline; the decode
+    its visible keys).  `prefill16k_sample` is the 16K prefill sample of cpu_baseline; the decode
     sample takes a few (sequence, head) slices copied from the device-resident cache."""
     import numpy as np
 
@@ -295,7 +295,7 @@ def oracle_per_config(c3_sample, gpu_ms, decode_inputs):
         w = pin.WORKLOADS[name]
         q, k, v, _ = pin.workload_inputs(w, "cpu")
         entry(name, "every row", w.pairs(), run(w, q, k, v, 0, w.H))
-    entry(PREFILL[0], c3_sample["sample"], c3_sample["_pairs"], c3_sample["_seconds"])
+    entry(PREFILL[0], prefill16k_sample["sample"], prefill16k_sample["_pairs"], prefill16k_sample["_seconds"])
     # 64K prefill: blocks of 512 rows at four places along the sequence, in two heads
     w = pin.WORKLOADS[PREFILL[1]]
     q, k, v, _ = pin.workload_inputs(w, "cpu")
