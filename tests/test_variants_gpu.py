@@ -227,20 +227,24 @@ def test_workload_variants_t65536(variant):
     compare(sub, ref, "bf16", decidable_rows(q, k, True, kw, variant, rows=rows), f"T=65536 {variant}")
 
 
+H8 = {key: val + val[::-1] for key, val in H4.items()}
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("name", sorted(VARIANTS))
-def test_decode_variant(name):
-    """Split-KV decode (one query head per KV head) and the grouped kernel (4 query heads
-    per KV head), several split counts; the oracle sees the query as the last row of a
-    causal problem."""
+def test_decode_variant(name, d):
+    """Split-KV decode (one query head per KV head) and the grouped kernel (4 and 8 query
+    heads per KV head: the lanes of a key split the heads), several split counts; the
+    oracle sees the query as the last row of a causal problem."""
     variant = VARIANTS[name]
-    for H, Hkv in ((4, 4), (4, 1)):
-        q, k, v, _ = pin.random_qkv(2, H, Hkv, 1, 700, 128, torch.bfloat16, seed=740 + H + Hkv)
-        ref = polar_attention_variant(to_np(q), to_np(k), to_np(v), causal=True, variant=variant, **H4)
-        ok = decidable_rows(q, k, True, H4, variant)
+    for H, Hkv, kw in ((4, 4, H4), (4, 1, H4), (8, 1, H8)):
+        q, k, v, _ = pin.random_qkv(2, H, Hkv, 1, 700, d, torch.bfloat16, seed=740 + H + Hkv + d)
+        ref = polar_attention_variant(to_np(q), to_np(k), to_np(v), causal=True, variant=variant, **kw)
+        ok = decidable_rows(q, k, True, kw, variant)
         for splits in (1, 3, 0):
-            out = pa.decode(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=splits, stats=True, variant=variant, **H4)
+            out = pa.decode(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=splits, stats=True, variant=variant, **kw)
             torch.cuda.synchronize()
-            compare(out, ref, "bf16", ok, f"decode {name} H={H} Hkv={Hkv} S={splits}")
+            compare(out, ref, "bf16", ok, f"decode {name} d={d} H={H} Hkv={Hkv} S={splits}")
 
 
 @pytest.mark.parametrize("name", ["window", "soft", "all", "qnorm"])
