@@ -265,13 +265,13 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
       } else {
         row = (size_t)key;
       }
+      // a key past the end (or in a skipped block) loads nothing: its score is -inf, so
+      // only its V row enters the sums, times a weight of 0, and that row still holds the
+      // zeros it started with or an earlier key's finite values of this sequence
       if (r.ok[u]) {
         const size_t off = (PAGED ? row * D : cont_off + row * D) + dch * 8;
         r.k[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));  // read once
         r.v[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
-      } else {
-        r.k[u] = u32x4{0, 0, 0, 0};
-        r.v[u] = u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -379,6 +379,8 @@ polar_decode_group_kernel(const GroupDecodeParams p) {
   };
 
   Rows ra, rb;
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) ra.k[u] = ra.v[u] = rb.k[u] = rb.v[u] = u32x4{0, 0, 0, 0};
   if constexpr (PAGED) table_entries(lo);
   issue(lo, ra);
   if constexpr (PAGED) table_entries(lo + STEP);
