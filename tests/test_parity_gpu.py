@@ -197,6 +197,51 @@ def test_fwd_maximum_key_count_closed_forms():
     assert got["stats"][0][1] == n and got["stats"][0][2] == n
 
 
+def test_decode_long_cache_closed_forms():
+    """Decode over a cache of 20,000,002 keys (past 2^24, where a count kept in fp32 by ones
+    would stop growing), through the one-head split kernel with the merge and through the
+    grouped kernel (two query heads over one KV head), against closed forms of the
+    definition: head 0 has q = 0 (every score 0: n_eff = n, u = normalize(sum_j v_j)); head
+    1 has q = a e_0 and only the last key has a component along e_0 (b e_0), so its score is
+    D = a b / sqrt(d) and every other score 0 (n_eff = S1^2 / S2 with S1 = 1 + (n-1) e^-D,
+    S2 = 1 + (n-1) e^-2D, u = normalize(v_last + e^-D sum_{j < last} v_j))."""
+    n, d, a, b = 20_000_002, 128, 16.0, 12.0
+    print(f"[parity] decode over n={n} keys", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(81)
+    v = torch.randn(1, 1, n, d, device=DEV, generator=g, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=DEV)
+    k[0, 0, n - 1, 0] = b
+    q = torch.zeros(1, 2, 1, d, dtype=torch.bfloat16, device=DEV)
+    q[0, 1, 0, 0] = a
+    grouped = pa.decode(q, k, v, null_bias=[0.0, 0.0], stats=True)
+    single = [pa.decode(q[:, h:h + 1].contiguous(), k, v, null_bias=[0.0], stats=True) for h in range(2)]
+    torch.cuda.synchronize()
+    total = torch.zeros(d, dtype=torch.float64)
+    step = 1 << 20
+    for s in range(0, n, step):
+        total += v[0, 0, s:min(n, s + step)].cpu().double().sum(0)
+    v_last = v[0, 0, n - 1].cpu().double()
+    del k, v
+    torch.cuda.empty_cache()
+    D = a * b / math.sqrt(d)
+    f = math.sqrt(2.0 * math.log(n))
+    s1 = 1.0 + (n - 1) * math.exp(-D)
+    s2 = 1.0 + (n - 1) * math.exp(-2.0 * D)
+    acc1 = v_last + math.exp(-D) * (total - v_last)
+    want_neff = [float(n), s1 * s1 / s2]
+    want_conf = [n / (n + math.exp(f)), s1 / (s1 + math.exp(f - D))]
+    want_dir = [(total / total.norm()).numpy(), (acc1 / acc1.norm()).numpy()]
+    cases = [("grouped", grouped, h, h) for h in range(2)] + [("split", single[h], 0, h) for h in range(2)]
+    for label, out, col, h in cases:
+        assert out["splits"] > 1, label
+        du = float(np.linalg.norm(to_np(out["direction"])[0, col, 0] - want_dir[h]))
+        dn = abs(float(out["n_eff"][0, col, 0]) - want_neff[h]) / want_neff[h]
+        dc = abs(float(out["confidence"][0, col, 0]) - want_conf[h])
+        print(f"[parity] long cache {label} head {h}: direction {du:.2e} n_eff {dn:.2e} confidence {dc:.2e} "
+              f"splits {out['splits']}", flush=True)
+        assert du <= 2e-2 and dn <= 1e-2 and dc <= 1e-2, (label, h, du, dn, dc)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [64, 128])
 def test_zero_values_give_zero_direction(dtype, d):
