@@ -63,10 +63,10 @@ def test_chunked_prefill_fp32_and_single_row_chunk():
 @pytest.mark.parametrize("B,H,T,chunk", [(1, 4, 2500, 1024), (2, 2, 3000, 700)])
 def test_chunked_over_cache_every_row(d, B, H, T, chunk):
     """Chunks as single forwards over the cache up to their last row (seq_q = chunk rows <
-    seq_k, causal aligned to the end of the keys): every row of every chunk against the
-    oracle's forward over the whole context."""
+    seq_k, causal aligned to the end of the keys), two query heads per KV head: every row of
+    every chunk against the oracle's forward over the whole context."""
     tau = [0.1 * (h + 1) for h in range(H)]
-    q, k, v, _ = pin.random_qkv(B, H, H, T, T, d, torch.bfloat16, 530 + d + chunk)
+    q, k, v, _ = pin.random_qkv(B, H, H // 2, T, T, d, torch.bfloat16, 530 + d + chunk)  # GQA: 2 per KV head
     ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=True, len_temp=tau)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     for c0 in range(0, T, chunk):
