@@ -188,31 +188,93 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
   }
 }
 
-// One wave per output row: merge S partial rows and form the channels.
-template <int D>
-__global__ __launch_bounds__(64) void polar_merge_kernel(const MergeParams p) {
+// Merge of S partial rows into one output row, and its channels.  NW waves per row: the
+// common maximum and the weighted S1, S2 are taken over the splits in parallel (split s by
+// thread s, s + 64 NW, ...), the value sums by wave w over the splits w, w + NW, ... (each
+// lane holding D / 64 dims), and the NW partial vectors are added in wave order through LDS,
+// so every result is the same on every run.  Rows with few splits take one wave, many-split
+// rows (few rows, long caches) four.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams p) {
   constexpr int W = D + 3;
   constexpr int DPL = D / 64;  // dims per lane
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const size_t row = blockIdx.x;  // (b * H + h) * Tq + i
   const int i = (int)(row % p.Tq);
   const int h = (int)((row / p.Tq) % p.H);
   const float* part = p.part + row * p.S * W;
+  __shared__ float red[2][NW];
+  __shared__ float acc_w[NW > 1 ? NW : 1][D];
 
+  // the common maximum
   float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, part[s * W]);
+  for (int s = tid; s < p.S; s += NW * 64) M = fmaxf(M, part[(size_t)s * W]);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
+  if constexpr (NW > 1) {
+    if (lane == 0) red[0][wave] = M;
+    __syncthreads();
+    M = red[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[0][w]);
+    __syncthreads();
+  }
+  // S1 and S2 brought to it (w for S1, w^2 for S2)
   float S1 = 0.0f, S2 = 0.0f;
+  for (int s = tid; s < p.S; s += NW * 64) {
+    const float* ps = part + (size_t)s * W;
+    const float ms = ps[0];
+    if (ms == -INFINITY) continue;  // a split without keys contributes nothing
+    const float w = expf(ms - M);
+    S1 = fmaf(w, ps[1], S1);
+    S2 = fmaf(w * w, ps[2], S2);  // squared correction factor
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    S1 += __shfl_xor(S1, sh, 64);
+    S2 += __shfl_xor(S2, sh, 64);
+  }
+  if constexpr (NW > 1) {
+    if (lane == 0) {
+      red[0][wave] = S1;
+      red[1][wave] = S2;
+    }
+    __syncthreads();
+    S1 = red[0][0];
+    S2 = red[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      S1 += red[0][w];
+      S2 += red[1][w];
+    }
+  }
+  // the value sums
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  for (int s = 0; s < p.S; ++s) {
-    const float ms = part[s * W];
-    if (ms == -INFINITY) continue;  // a split without keys contributes nothing
+#pragma unroll 4
+  for (int s = wave; s < p.S; s += NW) {
+    const float* ps = part + (size_t)s * W;
+    const float ms = ps[0];
+    if (ms == -INFINITY) continue;
     const float w = expf(ms - M);
-    S1 = fmaf(w, part[s * W + 1], S1);
-    S2 = fmaf(w * w, part[s * W + 2], S2);  // squared correction factor
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, part[s * W + 3 + lane + 64 * e], acc[e]);
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ps[3 + lane + 64 * e], acc[e]);
+  }
+  if constexpr (NW > 1) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc_w[wave][lane + 64 * e] = acc[e];
+    __syncthreads();
+    if (wave != 0) return;  // wave 0 finishes the row
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      float a = acc_w[0][lane + 64 * e];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) a += acc_w[w][lane + 64 * e];
+      acc[e] = a;
+    }
   }
   float nn = 0.0f;
 #pragma unroll

@@ -87,9 +87,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
   const int kv_end = CAUSAL ? min(Tk, q0 + BM + off) : Tk;
   const int ntiles = (kv_end + BN - 1) / BN;
   const int wave_kmax = CAUSAL ? min(wq0 + QPW - 1 + off, Tk - 1) : Tk - 1;
-  const int wave_kmin = CAUSAL ? min(wq0 + off, Tk - 1) : Tk - 1;
-  // tiles every row of the wave sees in full: the pipelined steps
-  const int n_full = min(ntiles, (wave_kmin + 1) / BN);
 
   // K of tiles 0 and 1 and V of tile 0 before anything else
   load_tile<D, BN, NW>(kb, 0, voff, k_buf0, wave);

@@ -300,10 +300,14 @@ constexpr int kSplitTargetGrouped = 2048;
 constexpr int kSplitTargetPaged = 6144;
 constexpr int kSplitMinKeys = 256;
 constexpr int kSplitMinKeysPaged = 2048;
+// at most this many splits: past it, fewer rows gain less from more workgroups than the
+// partial rows and their merge cost (batch 1, 8 heads, 2^20 keys: 128 splits 0.634 ms,
+// 512 splits 0.699 ms; 64K keys: 0.060 against 0.072 ms at 256)
+constexpr int kSplitMax = 128;
 
 int auto_splits(const polar_problem* pr, bool paged) {
   // About the target's number of split workgroups, with at least the minimum of keys per
-  // split (one split when the sequence is shorter).  A
+  // split (one split when the sequence is shorter) and at most kSplitMax splits.  A
   // workgroup serves one query head, or a chunk of a query-head group when heads share a
   // KV head.
   const long long rows = (long long)pr->batch * (pr->heads / group_chunk(pr));
@@ -314,6 +318,7 @@ int auto_splits(const polar_problem* pr, bool paged) {
   const long long min_keys = paged ? kSplitMinKeysPaged : kSplitMinKeys;
   const long long max_by_len = (pr->seq_k + min_keys - 1) / min_keys;
   if (s > max_by_len) s = max_by_len;
+  if (s > kSplitMax) s = kSplitMax;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -436,7 +441,9 @@ template <int D>
 polar_status launch_merge(const polar_problem* pr, MergeParams& mp, void* stream) {
   const long long rows = (long long)pr->batch * pr->heads * pr->seq_q;
   if (rows > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-  return launch(polar::polar_merge_kernel<D>, dim3((unsigned)rows), dim3(64), mp, stream);
+  // four waves per row once the splits outnumber what one wave's lanes take in one pass
+  if (mp.S > 64) return launch(polar::polar_merge_kernel<D, 4>, dim3((unsigned)rows), dim3(256), mp, stream);
+  return launch(polar::polar_merge_kernel<D, 1>, dim3((unsigned)rows), dim3(64), mp, stream);
 }
 
 polar_status merge_with_lens(const polar_problem* pr, const float* partials, int32_t num_splits,

@@ -356,25 +356,29 @@ def test_grouped_auto_splits_count_group_chunks(lib):
     """A grouped workgroup serves up to 8 query heads of a group, so the automatic split
     count is sized by (batch x kv_heads x chunks) workgroups; it aims for 4096 split
     workgroups with one head per workgroup, 2048 with the grouped kernel over a contiguous
-    cache and 6144 over a paged pool, with splits of at least 256 keys (2048 paged)."""
-    mha = good_problem(batch=2, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
-    gqa = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
-    g3 = good_problem(batch=2, heads=6, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    cache and 6144 over a paged pool, with splits of at least 256 keys (2048 paged) and at
+    most 128 splits."""
+    mha = good_problem(batch=16, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    gqa = good_problem(batch=16, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    g3 = good_problem(batch=16, heads=6, kv_heads=2, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
+    few = good_problem(batch=2, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 20, causal=False, head_dim=128)
     n = {}
-    for name, prob in (("mha", mha), ("gqa", gqa), ("g3", g3)):
+    for name, prob in (("mha", mha), ("gqa", gqa), ("g3", g3), ("few", few)):
         pr, keep = prob.to_c()
         n[name] = lib.polar_attn_decode_num_splits(ctypes.byref(pr), 0)
-    assert n["mha"] == 4096 // 16          # 16 (b, h) rows
-    assert n["gqa"] == 2048 // 2 // 2 // 1  # 2 x 2 kv heads x 1 chunk of 4
-    assert n["g3"] == -(-2048 // (2 * 6))   # group of 3 runs one head per workgroup
+    assert n["mha"] == 4096 // 128           # 128 (b, h) rows
+    assert n["gqa"] == 2048 // 16 // 2 // 1  # 16 x 2 kv heads x 1 chunk of 4
+    assert n["g3"] == -(-2048 // (16 * 6))   # group of 3 runs one head per workgroup
+    assert n["few"] == 128                   # 4096 // 16 = 256 wanted, at most 128
     pr, keep = gqa.to_c()
-    kv = paged(num_blocks=1 << 17, max_blocks=1 << 16)
-    # paged: 6144 // 4 = 1536 splits wanted, but each keeps at least 2048 of the 2^20 keys
-    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == (1 << 20) // 2048
-    mid = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1 << 23, causal=False, head_dim=128)
+    kv = paged(num_blocks=1 << 21, max_blocks=1 << 16)
+    # paged: 6144 // 32 = 192 splits wanted, at most 128
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == 128
+    mid = good_problem(batch=16, heads=8, kv_heads=8, seq_q=1, seq_k=1 << 16, causal=False, head_dim=128)
     pr, keep = mid.to_c()
-    kv = paged(num_blocks=1 << 20, max_blocks=1 << 19)
-    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == 6144 // 4
+    kv = paged(num_blocks=1 << 16, max_blocks=1 << 12)
+    # 6144 // 128 = 48 splits wanted, and each keeps at least 2048 of the 2^16 keys: 32
+    assert lib.polar_attn_decode_paged_num_splits(ctypes.byref(pr), ctypes.byref(kv), 0) == (1 << 16) // 2048
     # at least 256 keys per split over a contiguous cache, 2048 over a paged pool
     short = good_problem(batch=2, heads=8, kv_heads=2, seq_q=1, seq_k=1000, causal=False, head_dim=128)
     pr, keep = short.to_c()
