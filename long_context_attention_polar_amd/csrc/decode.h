@@ -188,19 +188,90 @@ __global__ __launch_bounds__(NW * 64) void polar_decode_split_kernel(const Decod
   }
 }
 
+// Merge of few partial rows (at most 16 splits): one wave per output row, every lane walking
+// the splits in order with wave-uniform loads, then the channels.
+template <int D>
+__global__ __launch_bounds__(64) void polar_merge_few_kernel(const MergeParams p) {
+  constexpr int W = D + 3;
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b * H + h) * Tq + i
+  const int i = (int)(row % p.Tq);
+  const int h = (int)((row / p.Tq) % p.H);
+  const float* part = p.part + row * p.S * W;
+
+  float M = -INFINITY;
+  for (int s = 0; s < p.S; ++s) M = fmaxf(M, part[s * W]);
+  float S1 = 0.0f, S2 = 0.0f;
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+  for (int s = 0; s < p.S; ++s) {
+    const float ms = part[s * W];
+    if (ms == -INFINITY) continue;  // a split without keys contributes nothing
+    const float w = expf(ms - M);
+    S1 = fmaf(w, part[s * W + 1], S1);
+    S2 = fmaf(w * w, part[s * W + 2], S2);  // squared correction factor
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, part[s * W + 3 + lane + 64 * e], acc[e]);
+  }
+  float nn = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) nn = fmaf(acc[e], acc[e], nn);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) nn += __shfl_xor(nn, sh, 64);
+  const float inv = nn == 0.0f ? 0.0f : 1.0f / sqrtf(nn);  // a NaN norm stays NaN
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) p.dir[row * D + lane + 64 * e] = acc[e] * inv;
+  // the data-adaptive floor level needs the norm of the row's q (all lanes take part)
+  float sigma = 1.0f;
+  if (p.hp.level_form == POLAR_LEVEL_QNORM && p.q) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float x = (float)p.q[row * D + lane + 64 * e];
+      qq = fmaf(x, x, qq);
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) qq += __shfl_xor(qq, sh, 64);
+    sigma = p.scale * sqrtf(qq);
+  }
+  if (lane == 0) {
+    const int hpi = h * p.hp_stride;
+    int n = visible_keys(i, p.Tq, p.Tk, p.causal != 0);
+    if (p.lens) n = min(max(p.lens[row / ((size_t)p.H * p.Tq)], 0), p.Tk);
+    if (p.hp.window > 0) n = min(n, p.hp.window);
+    float neff = 0.0f, conf = 0.0f, count = 0.0f;
+    if (n > 0 && M > -INFINITY) {
+      const float lam = row_temperature(p.hp, hpi, n);
+      const float f = null_floor(p.hp, hpi, n, lam, sigma);
+      magnitude_channel(p.hp, hpi, M, S1, S2, f, p.floor_on != 0, neff, conf, count);
+    }  // a row that saw no key: direction 0 and all channels 0
+    p.neff[row] = neff;
+    if (p.conf) p.conf[row] = conf;
+    if (p.count) p.count[row] = count;
+    if (p.stats) {
+      p.stats[row * 3 + 0] = M;
+      p.stats[row * 3 + 1] = S1;
+      p.stats[row * 3 + 2] = S2;
+    }
+  }
+}
+
 // Merge of S partial rows into one output row, and its channels.  NW waves per row: the
 // common maximum and the weighted S1, S2 are taken over the splits in parallel (split s by
-// thread s, s + 64 NW, ...), the value sums by wave w over the splits w, w + NW, ... (each
-// lane holding D / 64 dims), and the NW partial vectors are added in wave order through LDS,
-// so every result is the same on every run.  Rows with few splits take one wave, many-split
-// rows (few rows, long caches) four.
+// thread s, s + 64 NW, ...),
+// the value sums by wave w over the splits w, w + NW, ... (each lane holding D / 64 dims),
+// and the NW partial vectors are added in wave order through LDS, so every result is the
+// same on every run.  Used past 16 splits (polar_merge_few_kernel below that): one wave,
+// four past 64.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams p) {
   constexpr int W = D + 3;
   constexpr int DPL = D / 64;  // dims per lane
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t row = blockIdx.x;  // (b * H + h) * Tq + i
   const int i = (int)(row % p.Tq);
   const int h = (int)((row / p.Tq) % p.H);
@@ -223,14 +294,15 @@ __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams 
   }
   // S1 and S2 brought to it (w for S1, w^2 for S2)
   float S1 = 0.0f, S2 = 0.0f;
-  for (int s = tid; s < p.S; s += NW * 64) {
+  auto add_split = [&](int s) __attribute__((always_inline)) {
     const float* ps = part + (size_t)s * W;
     const float ms = ps[0];
-    if (ms == -INFINITY) continue;  // a split without keys contributes nothing
+    if (ms == -INFINITY) return;  // a split without keys contributes nothing
     const float w = expf(ms - M);
     S1 = fmaf(w, ps[1], S1);
     S2 = fmaf(w * w, ps[2], S2);  // squared correction factor
-  }
+  };
+  for (int s = tid; s < p.S; s += NW * 64) add_split(s);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) {
     S1 += __shfl_xor(S1, sh, 64);
@@ -254,15 +326,16 @@ __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams 
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-#pragma unroll 4
-  for (int s = wave; s < p.S; s += NW) {
+  auto add_values = [&](int s) __attribute__((always_inline)) {
     const float* ps = part + (size_t)s * W;
     const float ms = ps[0];
-    if (ms == -INFINITY) continue;
+    if (ms == -INFINITY) return;
     const float w = expf(ms - M);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ps[3 + lane + 64 * e], acc[e]);
-  }
+  };
+#pragma unroll 4
+  for (int s = wave; s < p.S; s += NW) add_values(s);
   if constexpr (NW > 1) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc_w[wave][lane + 64 * e] = acc[e];

@@ -441,9 +441,11 @@ template <int D>
 polar_status launch_merge(const polar_problem* pr, MergeParams& mp, void* stream) {
   const long long rows = (long long)pr->batch * pr->heads * pr->seq_q;
   if (rows > INT32_MAX) return POLAR_ERR_UNSUPPORTED;
-  // four waves per row once the splits outnumber what one wave's lanes take in one pass
+  // up to 16 splits every lane walks them all; then the lanes share them, and four waves
+  // once they outnumber what one wave's lanes take in one pass
   if (mp.S > 64) return launch(polar::polar_merge_kernel<D, 4>, dim3((unsigned)rows), dim3(256), mp, stream);
-  return launch(polar::polar_merge_kernel<D, 1>, dim3((unsigned)rows), dim3(64), mp, stream);
+  if (mp.S > 16) return launch(polar::polar_merge_kernel<D, 1>, dim3((unsigned)rows), dim3(64), mp, stream);
+  return launch(polar::polar_merge_few_kernel<D>, dim3((unsigned)rows), dim3(64), mp, stream);
 }
 
 polar_status merge_with_lens(const polar_problem* pr, const float* partials, int32_t num_splits,
