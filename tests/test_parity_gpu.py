@@ -356,7 +356,8 @@ def decode_case(B, H, Hkv, Tk, d, seed, splits_list, tau=None, beta=None, kappa=
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_split_invariance(d):
-    decode_case(2, 4, 4, 3001, d, seed=40 + d, splits_list=[1, 2, 3, 8, 64, 0],
+    # 17 and 64 splits take the one-wave parallel merge, 65 and 300 the four-wave one
+    decode_case(2, 4, 4, 3001, d, seed=40 + d, splits_list=[1, 2, 3, 8, 17, 64, 65, 300, 0],
                 tau=[0.0, 0.1, 0.2, 0.05], beta=[0.0, -1.0, 2.0, 0.0], kappa=[1.0, 2.0, 1.0, 4.0])
 
 
