@@ -20,7 +20,8 @@ already resident in HBM:
     prefill, the T=65536 prefill as a chunked
     prefill (8 chunks of 8192 queries: partial forwards over the cached prefix and over
     the chunk, merged), and under two reading variants (a per-key soft floor; a sliding
-    window of 4096 keys).
+    window of 4096 keys), and the decode latency at batch 1 (the first sequence of the
+    decode cache alone).
 `value` is the prefill throughput in TFLOP/s: the algorithmic flops of the two prefill
 launches (4 d per computed causal (query, key) pair) over their HIP-event time.  The
 decode bandwidth is reported beside it.  Per-launch durations come from HIP events
@@ -30,6 +31,7 @@ launches on).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -46,6 +48,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PREFILL = ["bf16_b1_h16_t16384_d128_groups", "bf16_b1_h16_t65536_d64_lentemp"]
 DECODE = "bf16_decode_b64_h8_tk65536_d128"
 PAGED = "bf16_paged_decode_b64_h32_kv8_tk65536_d128"
+DECODE_B1 = "bf16_decode_b1_h8_tk65536_d128"
 BWD = "bf16_bwd_b1_h16_kv4_t16384_d128"
 BWD_SAVED = BWD + "_saved"
 CHUNK = 8192
@@ -423,6 +426,17 @@ def main():
     kwd = dict(len_temp=wd.len_temp(), null_bias=wd.null_bias(), count_scale=wd.count_scale())
     parts.append(dict(name=DECODE, w=wd, kind="decode", bytes=decode_bytes(wd),
                       run=lambda: pa.decode(qd, kd, vd, workspace=ws, out=outd, **kwd)))
+    # decode latency at batch 1: the first sequence of the same cache, automatic splits,
+    # timed in a loop of its own
+    w1b = dataclasses.replace(wd, B=1)
+    q1b, k1b, v1b = qd[:1], kd[:1], vd[:1]
+    prob1b = pa.problem_for(q1b, k1b, causal=True, len_temp=wd.len_temp(), null_bias=wd.null_bias(),
+                            count_scale=wd.count_scale())
+    splits1b = pa.decode_num_splits(prob1b, 0)
+    ws1b = torch.empty(pa.decode_workspace_bytes(prob1b, 0), dtype=torch.uint8, device=dev)
+    out1b = pa.allocate_outputs(1, wd.H, 1, wd.d, dev)
+    parts.append(dict(name=DECODE_B1, w=w1b, kind="decode", bytes=decode_bytes(w1b), headline=False, separate=True,
+                      run=lambda: pa.decode(q1b, k1b, v1b, workspace=ws1b, out=out1b, **kwd)))
     wp = pin.WORKLOADS[PAGED]
     qp, kpool, vpool, table, lens = pin.paged_decode_inputs(wp, dev)
     probp = pa.Problem(wp.B, wp.H, wp.Hkv, 1, wp.Tk, wp.d, False, pa.POLAR_BF16)
@@ -506,7 +520,7 @@ def main():
             entry["gbs"] = p["bytes"] / (avg * 1e-3) / 1e9
             entry["frac_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS
             entry["bytes_per_launch"] = p["bytes"]
-            entry["splits"] = splits if p["name"] == DECODE else None
+            entry["splits"] = {DECODE: splits, DECODE_B1: splits1b}.get(p["name"])
         res[p["name"]] = entry
     assert torch.isfinite(outd["direction"]).all()  # a sanity check; parity is in the tests
 
@@ -545,6 +559,11 @@ def main():
                    "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
         "roofline": roofline,
         "decode": decode_roof,
+        "decode_batch1": {"bound": "hbm", "achieved": res[DECODE_B1]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": res[DECODE_B1]["frac_hbm_peak"], "us": res[DECODE_B1]["ms_avg"] * 1e3,
+                          "splits": splits1b,
+                          "note": "latency: one sequence, 8 heads, 64K keys (the first sequence of the decode "
+                                  "cache), split kernel and merge"},
         "paged_gqa_decode": {"bound": "hbm", "achieved": res[PAGED]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": res[PAGED]["frac_hbm_peak"], "ms": res[PAGED]["ms_avg"],
                              "traffic": measured_traffic("paged_gqa_decode_b64_h32_kv8_tk65536_d128"),
