@@ -513,3 +513,27 @@ def test_workload_decode_64k():
     print(f"[parity] decode max errors over all {w.B * w.H} rows {worst}", flush=True)
     del k, v
     torch.cuda.empty_cache()
+
+
+def test_workload_decode_batch1_latency_call():
+    """The batch-1 decode as the benchmark times it: the first sequence of the 64K decode
+    cache alone (the per-sequence generator makes B=1 draw exactly that sequence), automatic
+    split count, caller-given workspace and outputs, no statistics.  Its 128 splits take the
+    four-wave merge; all 8 rows against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(pin.WORKLOADS["bf16_decode_b64_h8_tk65536_d128"], B=1)
+    print("[parity] batch-1 decode, first sequence of the decode workload", flush=True)
+    q, k, v, _ = pin.workload_inputs(w, DEV)
+    kw = dict(len_temp=w.len_temp(), null_bias=w.null_bias(), count_scale=w.count_scale())
+    prob = pa.problem_for(q, k, causal=True, **kw)
+    splits = pa.decode_num_splits(prob, 0)
+    assert splits > 64, splits  # the many-split merge
+    ws = torch.empty(pa.decode_workspace_bytes(prob, 0), dtype=torch.uint8, device=DEV)
+    out = pa.allocate_outputs(1, w.H, 1, w.d, DEV)
+    res = pa.decode(q, k, v, workspace=ws, out=out, **kw)
+    torch.cuda.synchronize()
+    assert res["splits"] == splits
+    ref = polar_attention(to_np(q), to_np(k), to_np(v), causal=True, **kw)
+    sub = {key: t for key, t in res.items() if torch.is_tensor(t) and key != "partials"}
+    e = assert_parity(sub, ref, "bf16", label="batch-1 decode")
+    print(f"[parity] batch-1 decode ({splits} splits) max errors over its {w.H} rows {e}", flush=True)
