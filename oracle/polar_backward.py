@@ -16,6 +16,13 @@ The row maximum cancels in every output, so the quantities below use p_j = P_j /
                               d count / d conf = T,  d count / d n_eff = conf (1 - T^2) / (kappa n_eff)
     dP_j/ds_j = P_j,  ds/dq = lam scale k,  ds/dk = lam scale q   (lam depends on n only)
 
+The same map holds under the reading variants that change only per-row constants
+(polar_variants; [ATMA §2.1] names the parts without formulas): the temperature forms
+change lam(n), the floor levels "gauss" and "gumbel2" change f(n) (both depend on the
+count n alone, not on q or k), and the saturation "log1p" has T = tanh(ln(1 + n_eff) /
+kappa), so d count / d n_eff = conf (1 - T^2) / (kappa (1 + n_eff)).  A per-key floor, a
+window or the q-scaled floor level change the map itself and are not covered here.
+
 Given upstream gradients g_u, g_n, g_c, g_k of one row:
 
     G_conf = g_c + g_k T,   G_neff = g_n + g_k conf (1 - T^2) / (kappa n_eff)
@@ -33,6 +40,7 @@ from __future__ import annotations
 import numpy as np
 
 from .polar_oracle import length_temperature, null_floor, visible_count
+from .polar_variants import floor_level, temperature, variant_of
 
 __all__ = ["polar_attention_backward", "row_coefficients"]
 
@@ -41,9 +49,10 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def row_coefficients(m, s1, s2, acc, n, lam, beta, kappa, g_u, g_n, g_c, g_k):
+def row_coefficients(m, s1, s2, acc, n, lam, beta, kappa, g_u, g_n, g_c, g_k, f=None, saturation="log"):
     """c1, c2 [R] and w [R, d] of the rows from their statistics (relative to e^m) and the
-    upstream gradients (see the module docstring)."""
+    upstream gradients (see the module docstring).  f: the rows' null floor when it is not
+    reading R's lam sqrt(2 ln n) + beta; saturation: "log" or "log1p"."""
     s1, s2, acc = _f64(s1), _f64(s2), _f64(acc)
     n_eff = s1 * s1 / s2
     norm = np.sqrt(np.sum(acc * acc, axis=-1))
@@ -53,12 +62,17 @@ def row_coefficients(m, s1, s2, acc, n, lam, beta, kappa, g_u, g_n, g_c, g_k):
         conf = np.ones_like(s1)
         dconf_dz1 = np.zeros_like(s1)
     else:
-        f = null_floor(n, lam, beta)
+        f = null_floor(n, lam, beta) if f is None else _f64(f)
         conf = 1.0 / (1.0 + np.exp(f - _f64(m) - np.log(s1)))
         dconf_dz1 = conf * (1.0 - conf)
-    t = np.tanh(np.log(n_eff) / kappa)
+    if saturation == "log1p":
+        t = np.tanh(np.log1p(n_eff) / kappa)
+        slope = (1.0 - t * t) / (kappa * (1.0 + n_eff))
+    else:
+        t = np.tanh(np.log(n_eff) / kappa)
+        slope = (1.0 - t * t) / (kappa * n_eff)
     g_conf = g_c + g_k * t
-    g_neff = g_n + g_k * conf * (1.0 - t * t) / (kappa * n_eff)
+    g_neff = g_n + g_k * conf * slope
     c1 = (2.0 * g_neff * n_eff + g_conf * dconf_dz1) / s1
     c2 = -g_neff * n_eff / s2
     w = np.where(norm[:, None] > 0.0, (g_u - u * np.sum(u * g_u, axis=-1, keepdims=True)) / safe[:, None], 0.0)
@@ -66,14 +80,19 @@ def row_coefficients(m, s1, s2, acc, n, lam, beta, kappa, g_u, g_n, g_c, g_k):
 
 
 def polar_attention_backward(q, k, v, grads, *, causal: bool = True, len_temp=None, null_bias=None,
-                             count_scale=None, softmax_scale=None):
+                             count_scale=None, softmax_scale=None, variant=None):
     """Gradients of sum(g_u . u) + sum(g_n n_eff) + sum(g_c conf) + sum(g_k count) with
     respect to q, k, v (fp64).
 
     q [B,H,Tq,d], k and v [B,Hkv,Tk,d]; grads: dict with any of "direction" [B,H,Tq,d],
-    "n_eff", "confidence", "count" [B,H,Tq] (missing entries are zero).
+    "n_eff", "confidence", "count" [B,H,Tq] (missing entries are zero).  variant: a dict
+    of polar_variants keys; only the temperature, the floor levels "gauss" and "gumbel2"
+    and the saturation may differ from reading R.
     Returns dict dq [B,H,Tq,d], dk, dv [B,Hkv,Tk,d].
     """
+    var = variant_of(variant)
+    if var["key_floor"] != "null" or var["window"] or var["floor_level"] == "qnorm":
+        raise ValueError("gradients cover the variants that change only per-row constants")
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
@@ -98,7 +117,13 @@ def polar_attention_backward(q, k, v, grads, *, causal: bool = True, len_temp=No
             tau = 0.0 if len_temp is None else float(len_temp[h])
             beta = None if null_bias is None else float(null_bias[h])
             kappa = 1.0 if count_scale is None else float(count_scale[h])
-            lam = length_temperature(n, tau)
+            if var["temperature"] == "log":
+                lam = length_temperature(n, tau)
+            else:
+                lam = np.array([temperature(int(ni), tau, var) for ni in n])
+            f = None
+            if beta is not None and var["floor_level"] != "gauss":
+                f = lam * np.array([floor_level(int(ni), var) for ni in n]) + beta
             ls = lam * scale
             s = np.where(visible, ls[:, None] * (q[b, h] @ k[b, hk].T), -np.inf)
             m = s.max(axis=1)
@@ -107,7 +132,7 @@ def polar_attention_backward(q, k, v, grads, *, causal: bool = True, len_temp=No
             s2 = (p * p).sum(axis=1)
             acc = p @ v[b, hk]
             c1, c2, w = row_coefficients(m, s1, s2, acc, n, lam, beta, kappa, g_u[b, h], g_n[b, h], g_c[b, h],
-                                         g_k[b, h])
+                                         g_k[b, h], f=f, saturation=var["saturation"])
             ds = p * (c1[:, None] + 2.0 * c2[:, None] * p + w @ v[b, hk].T)
             dq[b, h] = ls[:, None] * (ds @ k[b, hk])
             dk[b, hk] += (ls[:, None] * ds).T @ q[b, h]

@@ -5,7 +5,7 @@ import importlib.util
 import pytest
 
 import oracle.polar_backward as good
-from tests.test_backward_oracle import CASES, fd_check
+from tests.test_backward_oracle import CASES, VARIANT_CASES, fd_check
 
 SRC = open(good.__file__).read()
 
@@ -16,8 +16,13 @@ MUTATIONS = {
     "dv weighted by ds": ("dv[b, hk] += p.T @ w", "dv[b, hk] += ds.T @ w"),
     "n_eff derivative sign": ("c2 = -g_neff * n_eff / s2", "c2 = g_neff * n_eff / s2"),
     "confidence derivative without (1 - conf)": ("dconf_dz1 = conf * (1.0 - conf)", "dconf_dz1 = conf"),
-    "count ignores the saturation slope": ("g_neff = g_n + g_k * conf * (1.0 - t * t) / (kappa * n_eff)",
-                                           "g_neff = g_n"),
+    "count ignores the saturation slope": ("g_neff = g_n + g_k * conf * slope", "g_neff = g_n"),
+    "log1p saturation with the slope of ln": ("slope = (1.0 - t * t) / (kappa * (1.0 + n_eff))",
+                                              "slope = (1.0 - t * t) / (kappa * n_eff)"),
+    "variant temperature ignored": ("lam = np.array([temperature(int(ni), tau, var) for ni in n])",
+                                    "lam = length_temperature(n, tau)"),
+    "gumbel2 floor level ignored": ("f = lam * np.array([floor_level(int(ni), var) for ni in n]) + beta",
+                                    "f = None"),
 }
 
 
@@ -34,9 +39,9 @@ def _mutant(old, new):
 def test_finite_differences_catch(name):
     mod = _mutant(*MUTATIONS[name])
     caught = False
-    for case in CASES:
+    for variant, case in [(None, c) for c in CASES] + VARIANT_CASES:
         try:
-            fd_check(mod, case)
+            fd_check(mod, case, variant=variant)
         except AssertionError:
             caught = True
             break

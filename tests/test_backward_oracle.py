@@ -15,6 +15,7 @@ import torch
 
 import oracle.polar_backward as pb_default
 from oracle import polar_attention
+from oracle.polar_variants import polar_attention_variant
 
 CASES = [
     # B, H, Hkv, Tq, Tk, d, causal, tau, beta, kappa
@@ -24,8 +25,25 @@ CASES = [
 ]
 
 
-def loss(q, k, v, gr, causal, tau, beta, kappa):
-    out = polar_attention(q, k, v, causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa)
+# the reading variants that change only per-row constants, each with a case whose length
+# temperatures are all positive (tau ln n with tau = 0 would zero every logit)
+VARIANT_CASES = [
+    ({"temperature": "ssmax", "saturation": "log1p"},
+     (1, 2, 1, 6, 6, 4, True, [0.5, 0.8], [0.0, -1.0], [1.0, 2.0])),
+    ({"temperature": "train_ratio", "train_len": 16, "floor_level": "gumbel2"},
+     (2, 2, 2, 5, 7, 3, True, [0.1, 0.0], [0.5, -0.5], [2.0, 1.0])),
+    ({"floor_level": "gumbel2", "saturation": "log1p"},
+     (1, 3, 3, 4, 9, 5, False, [0.2, 0.0, 0.1], [1.5, 0.0, -0.5], [1.0, 4.0, 1.0])),
+    ({"saturation": "log1p"}, (1, 2, 1, 6, 6, 4, True, [0.0, 0.3], None, [1.0, 0.5])),
+]
+
+
+def loss(q, k, v, gr, causal, tau, beta, kappa, variant=None):
+    if variant is None:
+        out = polar_attention(q, k, v, causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa)
+    else:
+        out = polar_attention_variant(q, k, v, causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa,
+                                      variant=variant)
     return float(np.sum(gr["direction"] * out["direction"]) + np.sum(gr["n_eff"] * out["n_eff"]) +
                  np.sum(gr["confidence"] * out["confidence"]) + np.sum(gr["count"] * out["count"]))
 
@@ -40,10 +58,12 @@ def case_inputs(B, H, Hkv, Tq, Tk, d, seed):
     return q, k, v, gr, r
 
 
-def fd_check(mod, case, seed=0, eps=1e-5, tol=1e-6):
+def fd_check(mod, case, seed=0, eps=1e-5, tol=1e-6, variant=None):
     B, H, Hkv, Tq, Tk, d, causal, tau, beta, kappa = case
     q, k, v, gr, r = case_inputs(B, H, Hkv, Tq, Tk, d, seed)
-    g = mod.polar_attention_backward(q, k, v, gr, causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa)
+    kw = {} if variant is None else {"variant": variant}
+    g = mod.polar_attention_backward(q, k, v, gr, causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa,
+                                     **kw)
     worst = 0.0
     for name, x in (("dq", q), ("dk", k), ("dv", v)):
         for _ in range(3):
@@ -54,8 +74,8 @@ def fd_check(mod, case, seed=0, eps=1e-5, tol=1e-6):
             lo = dict(args)
             hi[key] = x + eps * delta
             lo[key] = x - eps * delta
-            num = (loss(hi["q"], hi["k"], hi["v"], gr, causal, tau, beta, kappa) -
-                   loss(lo["q"], lo["k"], lo["v"], gr, causal, tau, beta, kappa)) / (2 * eps)
+            num = (loss(hi["q"], hi["k"], hi["v"], gr, causal, tau, beta, kappa, variant) -
+                   loss(lo["q"], lo["k"], lo["v"], gr, causal, tau, beta, kappa, variant)) / (2 * eps)
             ana = float(np.sum(g[name] * delta))
             err = abs(num - ana) / max(1.0, abs(num))
             worst = max(worst, err)
@@ -66,6 +86,35 @@ def fd_check(mod, case, seed=0, eps=1e-5, tol=1e-6):
 @pytest.mark.parametrize("case", CASES)
 def test_backward_matches_finite_differences(case):
     fd_check(pb_default, case)
+
+
+@pytest.mark.parametrize("variant,case", VARIANT_CASES, ids=[str(v) for v, _ in VARIANT_CASES])
+def test_backward_variant_matches_finite_differences(variant, case):
+    """Under the row-constant reading variants the gradient oracle is the derivative of
+    the variant forward oracle (an independent row-by-row definition)."""
+    fd_check(pb_default, case, variant=variant)
+
+
+def test_backward_default_variant_is_reading_r():
+    """An explicit default variant gives the same gradients as none."""
+    case = CASES[0]
+    B, H, Hkv, Tq, Tk, d, causal, tau, beta, kappa = case
+    q, k, v, gr, _ = case_inputs(B, H, Hkv, Tq, Tk, d, 3)
+    kw = dict(causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa)
+    a = pb_default.polar_attention_backward(q, k, v, gr, **kw)
+    b = pb_default.polar_attention_backward(q, k, v, gr, variant={"temperature": "log", "floor_level": "gauss",
+                                                                  "saturation": "log"}, **kw)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("variant", [{"key_floor": "soft"}, {"window": 4}, {"floor_level": "qnorm"}])
+def test_backward_rejects_variants_that_change_the_map(variant):
+    B, H, Hkv, Tq, Tk, d, causal, tau, beta, kappa = CASES[0]
+    q, k, v, gr, _ = case_inputs(B, H, Hkv, Tq, Tk, d, 0)
+    with pytest.raises(ValueError):
+        pb_default.polar_attention_backward(q, k, v, gr, causal=True, len_temp=tau, null_bias=beta,
+                                            count_scale=kappa, variant=variant)
 
 
 def torch_forward(q, k, v, causal, tau, beta, kappa):
