@@ -355,8 +355,12 @@ size_t polar_attn_bwd_workspace_bytes(const polar_problem* problem);
  * dk and dv summed over the query heads that share a KV head.  Same problem rules as
  * polar_attn_fwd (bf16 or fp32 inputs, head_dim 64 or 128, causal or not).  fp32 inputs
  * run in fp32 on the vector ALUs (batch * heads <= 65535).  bf16 inputs run on the
- * matrix cores: the row statistics come from the forward kernel (bf16 weights), and
- * P, dS and w enter the products as bf16 with fp32 sums.  Outputs are DEVICE fp32, 16-byte aligned and
+ * matrix cores: the row statistics come from the forward kernel in partial mode, and
+ * P, dS and w enter the products as bf16 with fp32 sums.  Reading variants: every
+ * temperature form, the floor levels POLAR_LEVEL_GAUSS and POLAR_LEVEL_GUMBEL2 (they
+ * depend on the count only, like lam) and either saturation (POLAR_SAT_LOG1P: T = tanh(ln(1
+ * + n_eff) / kappa), and the 1 / n_eff in G_neff becomes 1 / (1 + n_eff)); a per-key
+ * floor, a window or POLAR_LEVEL_QNORM returns POLAR_ERR_UNSUPPORTED.  Outputs are DEVICE fp32, 16-byte aligned and
  * overwritten: dq [B, heads, seq_q, head_dim], dk and dv [B, kv_heads, seq_k, head_dim].
  * `workspace` (DEVICE, 16-byte aligned, polar_attn_bwd_workspace_bytes bytes) is
  * scratch owned by the call until the stream reaches its end.  No output or the

@@ -66,9 +66,11 @@ __device__ __forceinline__ void row_constants(const HeadParams& hp, int hpi, boo
     conf = 1.0f / (1.0f + expf(f - m_nat - logf(s1)));
     dconf = conf * (1.0f - conf);
   }
-  const float t = tanhf(logf(n_eff) * kinv);
+  // count = conf tanh(x / kappa), x = ln n_eff, or ln(1 + n_eff) under the log1p saturation
+  const bool l1p = hp.sat_form == POLAR_SAT_LOG1P;
+  const float t = tanhf((l1p ? log1pf(n_eff) : logf(n_eff)) * kinv);
   const float g_conf = g_c + g_k * t;
-  const float g_neff = g_n + g_k * conf * (1.0f - t * t) * kinv / n_eff;
+  const float g_neff = g_n + g_k * conf * (1.0f - t * t) * kinv / (l1p ? 1.0f + n_eff : n_eff);
   c1 = (2.0f * g_neff * n_eff + g_conf * dconf) / s1;
   c2 = -g_neff * n_eff / s2;
 }

@@ -116,11 +116,6 @@ polar_status variant_params(const polar_problem* pr, HeadParams& hp) {
   return POLAR_OK;
 }
 
-bool default_variant(const HeadParams& hp) {
-  return hp.lam_form == POLAR_TEMP_LOG && hp.level_form == POLAR_LEVEL_GAUSS && hp.key_floor == POLAR_KEY_FLOOR_NULL &&
-         hp.sat_form == POLAR_SAT_LOG && hp.window == 0;
-}
-
 // Per-head tables -> kernel constants.  Checks the values the maths needs: finite
 // parameters, kappa > 0, and a non-negative length temperature over the visible counts
 // 1..seq_k, positive from n = 2 on (lam is affine in ln n, so checking n = seq_k suffices
@@ -189,7 +184,12 @@ enum class Entry { kFwd, kPartial, kDecode, kMerge, kBwd };
 polar_status check_entry_variant(const polar_problem* pr, const HeadParams& hp, Entry e, bool have_q) {
   switch (e) {
     case Entry::kBwd:
-      return default_variant(hp) ? POLAR_OK : POLAR_ERR_UNSUPPORTED;
+      // the variants that change only per-row constants (temperature, floor level from the
+      // count alone, saturation); a per-key floor, a window or the q-scaled level would
+      // change the gradient's form
+      return hp.key_floor == POLAR_KEY_FLOOR_NULL && hp.window == 0 && hp.level_form != POLAR_LEVEL_QNORM
+                 ? POLAR_OK
+                 : POLAR_ERR_UNSUPPORTED;
     case Entry::kFwd:
       return hp.window > 0 && !pr->causal ? POLAR_ERR_UNSUPPORTED : POLAR_OK;
     case Entry::kPartial:

@@ -510,12 +510,18 @@ def test_variant_enum_and_entry_checks(lib):
     pr, keep = problem(fl=2)
     o = outputs()
     assert lib.polar_attn_merge(ctypes.byref(pr), fake(4), 2, ctypes.byref(o), None) == 3
-    # the backward computes the default reading only
-    for v in (dict(kf=1), dict(w=4), dict(sat=1), dict(t=2), dict(fl=1)):
+    # the backward takes the variants that change only per-row constants: a per-key floor,
+    # a window or the data-adaptive level is unsupported; the others pass the variant check
+    # and stop at the alias check (dq given k's address), so nothing is launched
+    g = pa.PolarGrads(None, None, None, None)
+    for v in (dict(kf=1), dict(kf=2), dict(w=4), dict(fl=2)):
         pr, keep = problem(**v)
-        g = pa.PolarGrads(None, None, None, None)
         assert lib.polar_attn_bwd(ctypes.byref(pr), fake(1), fake(2), fake(3), ctypes.byref(g), fake(4), fake(5),
                                   fake(6), fake(7), 1 << 30, None) == 3, v
+    for v in (dict(), dict(sat=1), dict(t=1), dict(t=2), dict(fl=1), dict(t=1, fl=1, sat=1)):
+        pr, keep = problem(**v)
+        assert lib.polar_attn_bwd(ctypes.byref(pr), fake(1), fake(2), fake(3), ctypes.byref(g), fake(2), fake(5),
+                                  fake(6), fake(7), 1 << 30, None) == 7, v
 
 
 def test_python_binding_checks():

@@ -49,16 +49,19 @@ def compare(out, ref, label, tol=BWD_TOL):
     return errs
 
 
-def bwd_case(B, H, Hkv, Tq, Tk, d, dtype, causal, seed, tau=None, beta=None, kappa=None, names=ALL, scale=None):
+def bwd_case(B, H, Hkv, Tq, Tk, d, dtype, causal, seed, tau=None, beta=None, kappa=None, names=ALL, scale=None,
+             variant=None):
     label = f"B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} {dtype} causal={causal} grads={names}"
+    if variant:
+        label += f" variant={variant}"
     print(f"[bwd] {label}", flush=True)
     q, k, v, _ = pin.random_qkv(B, H, Hkv, Tq, Tk, d, dtype, seed)
     gr = pin.random_grads(B, H, Tq, d, seed + 7, names)
     ref = polar_attention_backward(to_np(q), to_np(k), to_np(v), {n: t.double().numpy() for n, t in gr.items()},
                                    causal=causal, len_temp=tau, null_bias=beta, count_scale=kappa,
-                                   softmax_scale=scale)
+                                   softmax_scale=scale, variant=variant)
     out = pa.bwd(q.to(DEV), k.to(DEV), v.to(DEV), {n: t.to(DEV) for n, t in gr.items()}, causal=causal,
-                 len_temp=tau, null_bias=beta, count_scale=kappa, softmax_scale=scale)
+                 len_temp=tau, null_bias=beta, count_scale=kappa, softmax_scale=scale, variant=variant)
     torch.cuda.synchronize()
     return compare(out, ref, label, BWD_TOL if dtype == torch.float32 else BWD_TOL_BF16)
 
@@ -76,6 +79,43 @@ def test_bwd_against_oracle(d, dtype, causal):
     temperature, floor and saturation."""
     Tq, Tk = (150, 150) if causal else (70, 201)
     bwd_case(2, 4, 2, Tq, Tk, d, dtype, causal, seed=500 + d + causal, tau=TAU4, beta=BETA4, kappa=KAPPA4)
+
+
+# the reading variants that change only per-row constants (temperature, count-only floor
+# level, saturation); tau ln n needs positive tau to keep the logits
+BWD_VARIANTS = {
+    "ssmax": (dict(temperature="ssmax"), [0.3, 0.5, 0.2, 0.4]),
+    "train_ratio": (dict(temperature="train_ratio", train_len=64), TAU4),
+    "gumbel2": (dict(floor_level="gumbel2"), TAU4),
+    "log1p": (dict(saturation="log1p"), TAU4),
+    "combined": (dict(temperature="ssmax", floor_level="gumbel2", saturation="log1p"), [0.3, 0.5, 0.2, 0.4]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_VARIANTS))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bwd_variant_against_oracle(name, d, dtype):
+    """The backward under each reading variant it supports, against the gradient oracle
+    under the same variant (causal, ragged tails, GQA groups of 2)."""
+    variant, tau = BWD_VARIANTS[name]
+    bwd_case(2, 4, 2, 150, 150, d, dtype, True, seed=700 + d, tau=tau, beta=BETA4, kappa=KAPPA4, variant=variant)
+
+
+def test_bwd_variant_non_causal_and_floor_off():
+    variant, tau = BWD_VARIANTS["combined"]
+    bwd_case(1, 4, 4, 70, 201, 64, torch.bfloat16, False, seed=733, tau=tau, beta=BETA4, kappa=KAPPA4,
+             variant=variant)
+    bwd_case(1, 4, 4, 100, 100, 128, torch.bfloat16, True, seed=734, tau=tau, beta=None, kappa=KAPPA4,
+             variant=variant)
+
+
+def test_bwd_rejects_variants_that_change_the_gradient():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16, device=DEV)
+    gr = {"n_eff": torch.zeros(1, 4, 8, device=DEV)}
+    for variant in (dict(key_floor="soft"), dict(key_floor="gate"), dict(window=4), dict(floor_level="qnorm")):
+        with pytest.raises(pa.PolarError):
+            pa.bwd(q, q, q, gr, null_bias=BETA4, variant=variant)
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -166,6 +206,23 @@ def test_bwd_saved_statistics_bitwise(B, H, Hkv, Tq, Tk, d, causal):
     gr = {n: t.to(DEV) for n, t in pin.random_grads(B, H, Tq, d, Tq + 3).items()}
     kw = dict(causal=causal, len_temp=[0.05 * (h % 3) for h in range(H)], null_bias=[0.5 * h - 1.0 for h in range(H)],
               count_scale=[1.0 + h for h in range(H)])
+    ref = pa.bwd(q, k, v, gr, **kw)
+    saved = pa.fwd_partial(q, k, v, **kw)
+    got = pa.bwd(q, k, v, gr, saved=saved, **kw)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(ref[key], got[key]), key
+
+
+def test_bwd_saved_statistics_bitwise_under_a_variant():
+    """The saved-statistics backward under a variant: the caller's partial forward takes
+    the same variant (its temperature sets the weights), and the results are bitwise those
+    of the self-contained call."""
+    variant, tau = BWD_VARIANTS["combined"]
+    q, k, v, _ = pin.random_qkv(1, 4, 2, 300, 300, 128, torch.bfloat16, seed=741)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    gr = {n: t.to(DEV) for n, t in pin.random_grads(1, 4, 300, 128, 742).items()}
+    kw = dict(causal=True, len_temp=tau, null_bias=BETA4, count_scale=KAPPA4, variant=variant)
     ref = pa.bwd(q, k, v, gr, **kw)
     saved = pa.fwd_partial(q, k, v, **kw)
     got = pa.bwd(q, k, v, gr, saved=saved, **kw)
