@@ -81,6 +81,23 @@ def test_graph_decode_with_workspace_and_merge():
     _check_replays(graph, gen, (q, k, v), out, lambda: pa.decode(q, k, v, **kw), "decode")
 
 
+@pytest.mark.parametrize("splits", [40, 100])
+def test_graph_decode_parallel_merge(splits):
+    """Explicit split counts past 16 and past 64: the merge runs over the splits in one
+    wave's lanes, and in four waves, inside the graph."""
+    B, H, Tk, d = 1, 8, 20000, 128
+    gen = torch.Generator().manual_seed(9110 + splits)
+    q, k, v = _static((B, H, 1, d)), _static((B, H, Tk, d)), _static((B, H, Tk, d))
+    _refill(gen, q, k, v)
+    kw = dict(len_temp=[0.05] * H, null_bias=[0.0] * H, num_splits=splits)
+    prob = pa.problem_for(q, k, causal=True, len_temp=kw["len_temp"], null_bias=kw["null_bias"])
+    assert pa.decode_num_splits(prob, splits) == splits
+    ws = torch.empty(pa.decode_workspace_bytes(prob, splits), dtype=torch.uint8, device=DEV)
+    out = pa.allocate_outputs(B, H, 1, d, DEV)
+    graph = _capture(lambda: pa.decode(q, k, v, workspace=ws, out=out, **kw))
+    _check_replays(graph, gen, (q, k, v), out, lambda: pa.decode(q, k, v, **kw), f"decode {splits} splits")
+
+
 def test_graph_decode_noalloc():
     B, H, Hkv, Tk, d = 4, 8, 8, 2500, 64
     gen = torch.Generator().manual_seed(9103)
