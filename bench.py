@@ -72,6 +72,8 @@ KERNEL_SOURCES = {
     "fwd_f32_b1_h2_t256_d64": (["fwd_f32.h"], "polar_fwd_f32_kernel"),
     "decode_b64_h8_tk65536_d128": (["decode.h"], "polar_decode_split_kernel"),
     "merge_b64_h8_d128": (["decode.h"], "polar_merge_few_kernel"),
+    "decode_b1_h8_tk65536_d128": (["decode.h"], "polar_decode_split_kernel"),
+    "merge_b1_h8_d128": (["decode.h"], "polar_merge_kernel"),
     "paged_gqa_decode_b64_h32_kv8_tk65536_d128": (["decode_group.h", "decode.h"], "polar_decode_group_kernel"),
     "bwd_dq_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dq_mfma_kernel"),
     "bwd_dkdv_b1_h16_kv4_t16384_d128": (["bwd_mfma.h", "bwd.h", "fwd_bf16.h"], "polar_bwd_dkdv_mfma_kernel"),

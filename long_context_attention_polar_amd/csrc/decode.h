@@ -279,9 +279,16 @@ __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams 
   __shared__ float red[2][NW];
   __shared__ float acc_w[NW > 1 ? NW : 1][D];
 
-  // the common maximum
-  float M = -INFINITY;
-  for (int s = tid; s < p.S; s += NW * 64) M = fmaxf(M, part[(size_t)s * W]);
+  // the common maximum; a thread's first split keeps its (m, S1, S2) in registers for the
+  // sums below, so they take no second round of loads
+  float m0 = -INFINITY, a0 = 0.0f, b0 = 0.0f;
+  if (tid < p.S) {
+    m0 = part[(size_t)tid * W];
+    a0 = part[(size_t)tid * W + 1];
+    b0 = part[(size_t)tid * W + 2];
+  }
+  float M = m0;
+  for (int s = tid + NW * 64; s < p.S; s += NW * 64) M = fmaxf(M, part[(size_t)s * W]);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
   if constexpr (NW > 1) {
@@ -294,15 +301,17 @@ __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams 
   }
   // S1 and S2 brought to it (w for S1, w^2 for S2)
   float S1 = 0.0f, S2 = 0.0f;
-  auto add_split = [&](int s) __attribute__((always_inline)) {
-    const float* ps = part + (size_t)s * W;
-    const float ms = ps[0];
+  auto add_split = [&](float ms, float s1, float s2) __attribute__((always_inline)) {
     if (ms == -INFINITY) return;  // a split without keys contributes nothing
     const float w = expf(ms - M);
-    S1 = fmaf(w, ps[1], S1);
-    S2 = fmaf(w * w, ps[2], S2);  // squared correction factor
+    S1 = fmaf(w, s1, S1);
+    S2 = fmaf(w * w, s2, S2);  // squared correction factor
   };
-  for (int s = tid; s < p.S; s += NW * 64) add_split(s);
+  if (tid < p.S) add_split(m0, a0, b0);
+  for (int s = tid + NW * 64; s < p.S; s += NW * 64) {
+    const float* ps = part + (size_t)s * W;
+    add_split(ps[0], ps[1], ps[2]);
+  }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) {
     S1 += __shfl_xor(S1, sh, 64);
@@ -326,16 +335,32 @@ __global__ __launch_bounds__(NW * 64) void polar_merge_kernel(const MergeParams 
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  auto add_values = [&](int s) __attribute__((always_inline)) {
-    const float* ps = part + (size_t)s * W;
-    const float ms = ps[0];
-    if (ms == -INFINITY) return;
-    const float w = expf(ms - M);
+  // A wave's splits are s = wave, wave + NW, ...  It loads the values of CH of them before
+  // it adds any, so those loads are in flight together, and adds them in split order.
+  constexpr int CH = 16;
+  for (int s0 = wave; s0 < p.S; s0 += NW * CH) {
+    float msv[CH], val[CH][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ps[3 + lane + 64 * e], acc[e]);
-  };
-#pragma unroll 4
-  for (int s = wave; s < p.S; s += NW) add_values(s);
+    for (int c = 0; c < CH; ++c) {
+      const int s = s0 + c * NW;
+      msv[c] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) val[c][e] = 0.0f;
+      if (s < p.S) {  // the same for the whole wave
+        const float* ps = part + (size_t)s * W;
+        msv[c] = ps[0];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) val[c][e] = ps[3 + lane + 64 * e];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (msv[c] == -INFINITY) continue;  // no keys, or past the last split
+      const float w = expf(msv[c] - M);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, val[c][e], acc[e]);
+    }
+  }
   if constexpr (NW > 1) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc_w[wave][lane + 64 * e] = acc[e];
